@@ -1,0 +1,152 @@
+"""Plain CPU model of the KV-cache control plane (test infrastructure only).
+
+Follows the BlockManager the pages describe (intelliparadigm article, section 3.2
+"PagedAttention"; lnwmold article, headings "Handling resource exhaustion",
+"From Sequences to Blocks", "Prefix Caching by hashing", "Control plane vs.
+data plane"):
+
+* a ``Block`` carries an id, a reference count and its token ids;
+* the manager keeps a deque of free blocks and a map of used ones and hands out
+  the free block at the head of the deque;
+* a sequence is cut into fixed-size blocks, never sharing a block with another
+  sequence except for a shared prefix, whose block ids are reused with their
+  reference counts raised;
+* freeing only marks a block free: its GPU contents are not cleared.
+
+Reading where the pages disagree: the printed ``allocate`` invents a new block id
+when the free deque is empty, which would grow a fixed pool without bound and
+clash with live ids; here the pool is fixed and allocation fails (returns None),
+which is when the scheduler preempts a sequence.  A freed block goes to the tail
+of the free deque.
+
+``plan_step`` turns a workload into the per-step metadata the data plane needs:
+block tables, the slot of every token written, cumulative sequence lengths for
+prefill ("Preparing for computation") and context lengths for decode.
+"""
+from __future__ import annotations
+
+from collections import deque
+
+import numpy as np
+
+__all__ = ["Block", "BlockManager", "slot_of", "cumulative_lengths", "plan_step"]
+
+
+class Block:
+    def __init__(self, block_id: int):
+        self.block_id = block_id
+        self.ref_count = 0
+        self.token_ids = []
+
+
+class BlockManager:
+    def __init__(self, num_blocks: int, free_order=None):
+        order = range(num_blocks) if free_order is None else [int(b) for b in free_order]
+        self.blocks = [Block(i) for i in range(num_blocks)]
+        self.free_blocks = deque(order)
+        self.used_blocks = {}
+
+    def allocate(self):
+        """Head of the free deque, reference count 1; None when the pool is empty."""
+        if not self.free_blocks:
+            return None
+        block_id = self.free_blocks.popleft()
+        block = self.blocks[block_id]
+        block.ref_count = 1
+        block.token_ids = []
+        self.used_blocks[block_id] = block
+        return block_id
+
+    def share(self, block_id: int) -> None:
+        """Reuse a cached block: one more reference, no copy."""
+        self.used_blocks[block_id].ref_count += 1
+
+    def free(self, block_id: int) -> None:
+        """Drop one reference; at zero the block returns to the free deque (not cleared)."""
+        block = self.used_blocks[block_id]
+        block.ref_count -= 1
+        if block.ref_count == 0:
+            del self.used_blocks[block_id]
+            self.free_blocks.append(block_id)
+
+
+def slot_of(table_row, position: int, block_size: int) -> int:
+    """Token ``position`` of a sequence lives in block table_row[position // block_size]
+    at offset position % block_size; its slot is block * block_size + offset."""
+    return int(table_row[position // block_size]) * block_size + position % block_size
+
+
+def cumulative_lengths(lengths) -> list:
+    """[0, l0, l0+l1, ...]."""
+    out = [0]
+    for n in lengths:
+        out.append(out[-1] + int(n))
+    return out
+
+
+def plan_step(wl, table_pad: int = -1) -> dict:
+    """Allocate every sequence's blocks in order and build the step's metadata.
+
+    Sequences take blocks from the free deque in index order; a sequence in a
+    prefix group other than the group's first reuses the first one's prefix
+    blocks (``share``) and allocates the rest.  Returns plain Python lists:
+
+    tables            per sequence, its block ids
+    history_slots     (seq, position, slot) of tokens written before the step
+    step_slots        (seq, position, slot) of the step's new tokens
+    prefill / decode  index lists of the sequences in each phase
+    cu_seqlens_q/k    over the prefill sequences
+    context_lens      over the decode sequences
+    block_tables      prefill and decode tables padded with ``table_pad`` to the
+                      widest table of the step
+    """
+    bs = wl.block_size
+    mgr = BlockManager(wl.num_blocks, wl.free_order)
+    tables = []
+    group_owner = {}
+    for i, s in enumerate(wl.seqs):
+        n_blocks = -(-s.context_len // bs)
+        table = []
+        if s.prefix_group >= 0 and s.prefix_group in group_owner:
+            owner_table = tables[group_owner[s.prefix_group]]
+            for j in range(s.prefix_len // bs):
+                mgr.share(owner_table[j])
+                table.append(owner_table[j])
+        elif s.prefix_group >= 0:
+            group_owner[s.prefix_group] = i
+        while len(table) < n_blocks:
+            b = mgr.allocate()
+            if b is None:
+                raise RuntimeError("pool exhausted")
+            table.append(b)
+        tables.append(table)
+
+    history, step = [], []
+    for i, s in enumerate(wl.seqs):
+        first = s.prefix_len if (s.prefix_group >= 0 and group_owner[s.prefix_group] != i) else 0
+        for p in range(first, s.history_len):
+            history.append((i, p, slot_of(tables[i], p, bs)))
+        for p in range(s.history_len, s.context_len):
+            step.append((i, p, slot_of(tables[i], p, bs)))
+
+    prefill = wl.prefill_seqs
+    decode = wl.decode_seqs
+    width = max([len(t) for t in tables] + [1])
+
+    def padded(idx):
+        return [tables[i] + [table_pad] * (width - len(tables[i])) for i in idx]
+
+    return {
+        "tables": tables,
+        "ref_counts": {b: blk.ref_count for b, blk in mgr.used_blocks.items()},
+        "history_slots": history,
+        "step_slots": step,
+        "prefill": prefill,
+        "decode": decode,
+        "cu_seqlens_q": cumulative_lengths(wl.seqs[i].new_tokens for i in prefill),
+        "cu_seqlens_k": cumulative_lengths(wl.seqs[i].context_len for i in prefill),
+        "context_lens": [wl.seqs[i].context_len for i in decode],
+        "prefill_block_tables": padded(prefill),
+        "decode_block_tables": padded(decode),
+        "table_width": width,
+    }
