@@ -1,0 +1,262 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged KV-cache hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--seed S]
+                    [--no-cpu-baseline] [--no-prefill]
+
+A step is one pass of the hot path over one batch of synthetic input: the KV
+write of the batch's new tokens (one per sequence), then paged decode of the
+batch: a 7B-shaped layer (32 q / 32 kv heads, head_dim 128, block_size 256),
+32 sequences with context lengths uniform on [512, 4096], block ids a random
+permutation of a pool 1.25x the used blocks, bf16 with fp32 accumulation.  All
+inputs are resident in device memory before the timed region; the K timed steps
+are bracketed by a device synchronisation on both sides.
+
+Printed: ONE JSON line.  ``value`` is the step's algorithmic HBM bytes (K and V
+of every context token, q, out, the new tokens' K/V read and written, and the
+metadata used) divided by the step time.  ``roofline`` is for the dominant
+kernel (decode), its duration measured with HIP events on its own stream
+inside the timed region.  ``prefill`` reports the varlen causal prefill (16 q /
+8 kv heads, 16 prompts of length uniform on [128, 2048]) in TFLOP/s over the
+unmasked causal pairs.  ``cpu_baseline`` times the CPU oracle on a bounded
+sample of the same decode workload, on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK_TFLOPS = 2516.6  # 256 CUs x 2.4 GHz x 4096 flop/clk/CU, dense
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="time only the prefill leg (for profiling it alone)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="rough CPU budget of the oracle baseline sample")
+    return ap.parse_args()
+
+
+def decode_bytes(wl, plan) -> int:
+    """K and V of every context token, q read, out written, context lengths and the
+    block-table entries actually used."""
+    s = wl.elem_bytes
+    ctx = [wl.seqs[i].context_len for i in plan.decode]
+    B = len(ctx)
+    blocks = sum(-(-L // wl.block_size) for L in ctx)
+    return (s * (2 * wl.num_kv_heads * wl.head_dim * sum(ctx) + 2 * B * wl.num_q_heads * wl.head_dim)
+            + 4 * (B + blocks))
+
+
+def store_bytes(wl, n_tokens: int) -> int:
+    """New tokens' K and V read and written, plus their slots."""
+    return 2 * 2 * n_tokens * wl.num_kv_heads * wl.head_dim * wl.elem_bytes + 4 * n_tokens
+
+
+def prefill_flops(wl, plan) -> int:
+    """QK^T and PV multiply-adds over the unmasked causal pairs only."""
+    pairs = 0
+    for i in plan.prefill:
+        s = wl.seqs[i]
+        Lq, Lk = s.new_tokens, s.context_len
+        pairs += Lq * (Lk - Lq) + Lq * (Lq + 1) // 2
+    return 4 * wl.head_dim * wl.num_q_heads * pairs
+
+
+def timed_steps(torch, pkv, fn, steps):
+    """Run fn `steps` times between two synchronisations with kernel timing on."""
+    pkv.timing_collect()
+    pkv.timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pkv.timing_enable(False)
+    return start.elapsed_time(end), wall, pkv.timing_collect()
+
+
+def cpu_baseline(wl, budget_s: float) -> dict:
+    """The CPU oracle, as it stands, on a bounded sample of the decode step: the KV
+    write of the step's new tokens, then decode of sequences in order until the
+    budget is spent (at least one)."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # noqa: BLE001 - threadpoolctl missing: report the affinity set
+        threads = len(os.sched_getaffinity(0))
+    plan = oracle.plan_step(wl)
+    hist = {"history_slots": plan["history_slots"], "step_slots": []}
+    k_cache, v_cache = oracle.build_caches(wl, hist)
+    step_rows = plan["step_slots"]
+    k_new = np.stack([wl.k[i][p] for (i, p, _) in step_rows])
+    v_new = np.stack([wl.v[i][p] for (i, p, _) in step_rows])
+    t0 = time.perf_counter()
+    oracle.store_kvcache(k_cache, v_cache, k_new, v_new, [s for (_, _, s) in step_rows])
+    done_bytes = store_bytes(wl, len(step_rows))
+    n = 0
+    s = wl.elem_bytes
+    passes = 0
+    while True:  # whole passes over the batch until the budget is spent
+        for b, i in enumerate(plan["decode"]):
+            q = wl.q[i][:1]
+            oracle.paged_decode(q, k_cache, v_cache, plan["decode_block_tables"][b:b + 1],
+                                plan["context_lens"][b:b + 1], wl.scale)
+            L = plan["context_lens"][b]
+            done_bytes += (s * (2 * wl.num_kv_heads * wl.head_dim * L
+                                + 2 * wl.num_q_heads * wl.head_dim)
+                           + 4 * (1 + -(-L // wl.block_size)))
+            n += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        passes += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    secs = time.perf_counter() - t0
+    return {"value": done_bytes / secs / 1e9, "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"KV write of the {len(step_rows)} new tokens + float64 decode of "
+                      f"{n} sequences ({passes} pass(es) over the {len(plan['decode'])}-sequence "
+                      f"batch, {secs:.1f} s)"}
+
+
+def prefill_leg(torch, pkv, workloads, DeviceStep, args) -> dict:
+    """Varlen causal prefill (16 prompts, lengths uniform on [128, 2048]) in TFLOP/s."""
+    wp = workloads.prefill_varlen(seed=args.seed)
+    ps = DeviceStep(wp, device="cuda", stale="nan")
+    for _ in range(3):
+        ps.run()
+    torch.cuda.synchronize()
+    _, _, pk = timed_steps(torch, pkv, ps.prefill, max(5, args.steps // 5))
+    pname = max((k for k in pk if "prefill" in k), key=lambda k: pk[k]["total_ms"])
+    flops = prefill_flops(wp, ps.plan)
+    tflops = flops / (pk[pname]["avg_ms"] * 1e-3) / 1e12
+    del ps
+    torch.cuda.empty_cache()
+    return {
+        "workload": "prefill_varlen_bf16: 16 prompts, lengths uniform [128, 2048], "
+                    "16 q / 8 kv heads, head_dim 128, block_size 256",
+        "kernel": pname, "bound": "mfma", "achieved": round(tflops, 2),
+        "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+        "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+        "algorithmic_flops_per_launch": flops, "avg_launch_ms": round(pk[pname]["avg_ms"], 5),
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
+              f"{world}): this library has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import paged_kv_cache_437_amd as pkv
+    import workloads
+    from paged_kv_cache_437_amd import _lib
+    from paged_kv_cache_437_amd.step import DeviceStep
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    if not os.path.exists(_lib.LIB_PATH):
+        from paged_kv_cache_437_amd.build import build
+        build()
+    _lib.load()
+
+    if args.prefill_only:
+        print(json.dumps({"prefill": prefill_leg(torch, pkv, workloads, DeviceStep, args)}),
+              flush=True)
+        return
+
+    # ---- decode step (the headline workload)
+    wl = workloads.decode_mha(seed=args.seed)
+    step = DeviceStep(wl, device="cuda", stale="nan")
+    plan = step.plan
+    n_new = len(plan.step_slots)
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+    ms_total, wall, kernels = timed_steps(torch, pkv, step.run, args.steps)
+    ms_per_step = ms_total / args.steps
+    d_bytes = decode_bytes(wl, plan)
+    s_bytes = store_bytes(wl, n_new)
+    value = (d_bytes + s_bytes) / (ms_per_step * 1e-3) / 1e9
+    decode_kernels = {k: v for k, v in kernels.items() if "decode" in k}
+    dom_name = max(decode_kernels, key=lambda k: decode_kernels[k]["total_ms"])
+    dom = decode_kernels[dom_name]
+    achieved = d_bytes / (dom["avg_ms"] * 1e-3) / 1e9
+
+    result = {
+        "metric": "paged decode HBM GB/s + prefill TFLOP/s, % of MI355X roofline",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode_mha_bf16: KV write of 1 new token/seq + paged decode; 32 seqs, "
+                        "ctx uniform [512, 4096], 32 q / 32 kv heads, head_dim 128, "
+                        "block_size 256, pool 1.25x used blocks, random block permutation",
+            "seed": args.seed,
+            "sum_context": int(sum(wl.seqs[i].context_len for i in plan.decode)),
+            "pool_blocks": wl.num_blocks,
+            "parallelism": "none (1 GPU)",
+        },
+        "roofline": {
+            "kernel": dom_name,
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": d_bytes,
+            "avg_launch_ms": round(dom["avg_ms"], 5),
+        },
+        "kernels": {k: {"launches": v["launches"], "avg_ms": round(v["avg_ms"], 5)}
+                    for k, v in kernels.items()},
+    }
+
+    # ---- varlen causal prefill, reported beside the decode line
+    if not args.no_prefill:
+        del step
+        torch.cuda.empty_cache()
+        result["prefill"] = prefill_leg(torch, pkv, workloads, DeviceStep, args)
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

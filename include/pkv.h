@@ -1,0 +1,168 @@
+/*
+ * pkv.h - paged KV-cache attention for AMD Instinct MI355X (gfx950).
+ *
+ * The data plane of a nano-vLLM-style engine: the KV write through a slot
+ * mapping, causal prefill over sequences packed by cumulative lengths that reads
+ * cached blocks through block tables, and decode over block tables with context
+ * lengths.  Pages: nano-vLLM, intelliparadigm article section 3.2
+ * "PagedAttention" (fixed pool of 256-token blocks, ref-counted ids, block reuse
+ * by prefix hash) and lnwmold article headings "From Sequences to Blocks",
+ * "Prefix Caching by hashing", "Control plane vs. data plane" (block metadata
+ * lives on the CPU, KV data on the GPU, freed blocks are not cleared),
+ * "Prefill and Decode" and "Preparing for computation" (prefill packs sequences
+ * by cumulative lengths; decode batches one token per sequence).
+ *
+ * Conventions for every call:
+ *  - Every array pointer is a DEVICE pointer owned by the caller.  The library
+ *    allocates no device memory, keeps no state between calls, never
+ *    synchronises, and enqueues all its work on `stream`.  Calls are reentrant.
+ *  - Element type: q, k, v, both caches and out share one type (pkv_dtype).
+ *    Metadata arrays are int32.
+ *  - Cache layout (one layer): k_cache and v_cache are each
+ *    [num_blocks][block_size][num_kv_heads][head_dim], contiguous.  Slot s is
+ *    block s / block_size, offset s % block_size, i.e. row s of
+ *    [num_blocks * block_size][num_kv_heads][head_dim].
+ *  - Grouped heads: q head h reads kv head h / (num_q_heads / num_kv_heads).
+ *  - Causal alignment: a sequence with Lq queries over Lk keys places query i
+ *    at position Lk - Lq + i; it sees keys 0 .. Lk - Lq + i.
+ *  - Host scalars are validated before any HIP call; a bad one returns an error
+ *    status and touches nothing.  Device arrays are the caller's contract and
+ *    are not read on the host (see each call).  Results never depend on cache
+ *    rows outside a sequence's (table, length): stale or NaN contents of freed
+ *    blocks and of the unused tail of a sequence's last block cannot leak.
+ *  - Supported: head_dim 64 or 128; block_size a power of two in [1, 256];
+ *    num_q_heads a multiple of num_kv_heads.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID = -1,     /* null pointer, negative size, inconsistent shapes */
+  PKV_ERR_UNSUPPORTED = -2, /* head_dim, block_size or dtype outside what is built */
+  PKV_ERR_WORKSPACE = -3,   /* decode workspace missing or too small */
+  PKV_ERR_HIP = -4          /* a kernel launch failed (hipGetLastError) */
+} pkv_status;
+
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+
+/* One layer's KV pool.  The control plane owns block ids and reference counts;
+ * the data plane sees ids only.  A block shared by several sequences (a cached
+ * prefix) simply appears in several block tables. */
+typedef struct {
+  void* k_cache; /* [num_blocks][block_size][num_kv_heads][head_dim] */
+  void* v_cache; /* same shape */
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t dtype; /* pkv_dtype */
+} pkv_cache;
+
+/* KV write (lnwmold, "Control plane vs. data plane": a reused block is simply
+ * overwritten).  For t in [0, num_tokens): if slot_mapping[t] >= 0, row
+ * slot_mapping[t] of each cache receives k[t] / v[t] bit for bit; slot -1 (a
+ * padding row) writes nothing.
+ *   k, v          [num_tokens][num_kv_heads][head_dim], contiguous
+ *   slot_mapping  [num_tokens] int32
+ * Contract: valid slots lie in [0, num_blocks * block_size) and are distinct
+ * within one call (two writes to one slot would race).  num_tokens == 0 is a
+ * no-op. */
+pkv_status pkv_store_kvcache(const pkv_cache* cache, const void* k, const void* v,
+                             const int32_t* slot_mapping, int32_t num_tokens,
+                             hipStream_t stream);
+
+/* Varlen causal prefill (lnwmold, "Preparing for computation": sequences are
+ * packed and addressed by cumulative lengths; "Prefix Caching": cached blocks
+ * are read, not recomputed).  Sequence b owns query rows
+ * cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 and Lk = cu_seqlens_k[b+1] -
+ * cu_seqlens_k[b] keys, read from the cache through block_tables[b]; K/V of all
+ * Lk tokens (the new ones included) must already be written.
+ *   q, out         [total_q][num_q_heads][head_dim], total_q = cu_seqlens_q[batch]
+ *   cu_seqlens_q   [batch+1] int32, non-decreasing, starting at 0
+ *   cu_seqlens_k   [batch+1] int32, non-decreasing, starting at 0
+ *   max_seqlen_q   host upper bound on every Lq (sizes the grid)
+ *   max_seqlen_k   host upper bound on every Lk
+ *   block_tables   [batch][block_table_stride] int32; only entries
+ *                  0 .. ceil(Lk / block_size)-1 of a row are read
+ *   scale          multiplies q.k before the softmax (usually 1/sqrt(head_dim))
+ * Contract: Lk >= Lq, Lk >= 1 when Lq > 0, ceil(Lk/block_size) <=
+ * block_table_stride, used table entries in [0, num_blocks).  Rows of out
+ * outside [0, total_q) are not written. */
+pkv_status pkv_paged_prefill(const pkv_cache* cache, const void* q, void* out,
+                             int32_t num_q_heads, int32_t batch,
+                             const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                             int32_t max_seqlen_q, int32_t max_seqlen_k,
+                             const int32_t* block_tables, int32_t block_table_stride,
+                             float scale, hipStream_t stream);
+
+/* Bytes of device workspace pkv_paged_decode needs for this shape (0 when a
+ * single split covers max_context_len).  num_splits as in pkv_paged_decode.
+ * Returns 0 for invalid arguments. */
+size_t pkv_paged_decode_workspace_size(const pkv_cache* cache, int32_t num_q_heads,
+                                       int32_t batch, int32_t max_context_len,
+                                       int32_t num_splits);
+
+/* Decode (lnwmold, "Prefill and Decode": one new token per sequence per step).
+ * Sequence b's single query attends to its context_lens[b] cached tokens, the
+ * new token's K/V (written beforehand) being the last.  Long contexts are cut
+ * at block boundaries into splits that run in parallel and are merged exactly
+ * (log-sum-exp) in a second kernel.
+ *   q, out          [batch][num_q_heads][head_dim]
+ *   context_lens    [batch] int32, each in [1, max_context_len]
+ *   max_context_len host upper bound on context_lens (sizes grid and workspace)
+ *   block_tables    [batch][block_table_stride] int32
+ *   workspace       device scratch of at least
+ *                   pkv_paged_decode_workspace_size(...) bytes (may be NULL when
+ *                   that size is 0); contents on entry are ignored
+ *   num_splits      0: split length chosen from max_context_len alone;
+ *                   S > 0: at most S splits per sequence
+ * The split boundaries depend only on lengths, never on block ids, so results
+ * are bit-identical under any relabelling of physical blocks. */
+pkv_status pkv_paged_decode(const pkv_cache* cache, const void* q, void* out,
+                            int32_t num_q_heads, int32_t batch,
+                            const int32_t* context_lens, int32_t max_context_len,
+                            const int32_t* block_tables, int32_t block_table_stride,
+                            float scale, void* workspace, size_t workspace_bytes,
+                            int32_t num_splits, hipStream_t stream);
+
+/* Kernel timing, off by default (tracing support for benchmarks).  While on,
+ * every kernel the library launches is bracketed by two hipEvents recorded on
+ * the stream it runs on.  pkv_timing_collect waits for the recorded events,
+ * writes one entry per kernel name (up to `capacity`) and returns how many
+ * kernel names there were, or a negative pkv_status on a HIP error; the
+ * recorded events are consumed.  Host-side bookkeeping only: no device memory. */
+typedef struct {
+  char kernel[64];
+  int64_t launches;
+  double total_ms;
+  double min_ms;
+  double max_ms;
+} pkv_kernel_timing;
+
+pkv_status pkv_timing_enable(int32_t on);
+int32_t pkv_timing_collect(pkv_kernel_timing* out, int32_t capacity);
+
+/* Static text for a status code. */
+const char* pkv_status_string(pkv_status status);
+
+/* Details of the last error returned on the calling thread ("" if none). */
+const char* pkv_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int32_t pkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

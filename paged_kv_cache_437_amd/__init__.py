@@ -1,0 +1,164 @@
+"""Paged KV-cache attention for AMD MI355X (gfx950): Python binding of libpkv.
+
+Three calls, the data plane of a nano-vLLM-style engine (nano-vLLM pages:
+intelliparadigm article section 3.2 "PagedAttention"; lnwmold article headings
+"From Sequences to Blocks", "Control plane vs. data plane", "Prefill and
+Decode", "Preparing for computation"):
+
+* ``store_kvcache``  - write new tokens' K/V into their slots;
+* ``paged_prefill``  - varlen causal attention over packed sequences, K/V read
+  from the cache through block tables (cached prefix blocks included);
+* ``paged_decode``   - one query per sequence over its cached context, split
+  over blocks and merged.
+
+This module only marshals arguments: shapes, dtypes and devices are checked,
+pointers and torch's current stream are handed to the C ABI, and every step of
+the computation runs in the HIP kernels.  There is no fallback: if libpkv.so is
+not built, the first call raises.
+
+Cache tensors are ``[num_blocks, block_size, num_kv_heads, head_dim]``
+(float32 or bfloat16); metadata tensors are int32 on the same device.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import PkvError
+
+__all__ = ["store_kvcache", "paged_prefill", "paged_decode", "paged_decode_workspace_size",
+           "PkvError", "version", "library_path", "timing_enable", "timing_collect"]
+
+_DTYPES = {torch.float32: _lib.PKV_F32, torch.bfloat16: _lib.PKV_BF16}
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+def version() -> int:
+    return _lib.load().pkv_version()
+
+
+def timing_enable(on: bool = True) -> None:
+    """Bracket every library kernel launch with HIP events on its stream (off by default)."""
+    _lib.check(_lib.load().pkv_timing_enable(1 if on else 0))
+
+
+def timing_collect() -> dict:
+    """{kernel name: {launches, total_ms, avg_ms, min_ms, max_ms}} since the last collect."""
+    lib = _lib.load()
+    buf = (_lib.PkvKernelTiming * 32)()
+    n = lib.pkv_timing_collect(buf, 32)
+    if n < 0:
+        _lib.check(n)
+    out = {}
+    for e in buf[:min(n, 32)]:
+        out[e.kernel.decode()] = {"launches": e.launches, "total_ms": e.total_ms,
+                                  "avg_ms": e.total_ms / max(e.launches, 1),
+                                  "min_ms": e.min_ms, "max_ms": e.max_ms}
+    return out
+
+
+def _cache_desc(k_cache: torch.Tensor, v_cache: torch.Tensor) -> _lib.PkvCache:
+    if k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache must both be [num_blocks, block_size, Hkv, D]")
+    if k_cache.dtype not in _DTYPES or v_cache.dtype != k_cache.dtype:
+        raise ValueError(f"cache dtype {k_cache.dtype} (float32 or bfloat16, both alike)")
+    for t in (k_cache, v_cache):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("caches must be contiguous device tensors")
+    nb, bs, hkv, d = k_cache.shape
+    return _lib.PkvCache(k_cache.data_ptr(), v_cache.data_ptr(), nb, bs, hkv, d,
+                         _DTYPES[k_cache.dtype])
+
+
+def _dev(t: torch.Tensor, name: str, dtype, like: torch.Tensor) -> int:
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != like.device or not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous on {like.device}")
+    return t.data_ptr()
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def store_kvcache(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor,
+                  v_cache: torch.Tensor, slot_mapping: torch.Tensor) -> None:
+    """k, v [N, Hkv, D] -> rows slot_mapping[t] of the caches (slot -1 skipped)."""
+    lib = _lib.load()
+    desc = _cache_desc(k_cache, v_cache)
+    n = slot_mapping.numel()
+    if k.shape != (n,) + tuple(k_cache.shape[2:]) or v.shape != k.shape:
+        raise ValueError(f"k, v must be [{n}, Hkv, D] like the cache rows")
+    args = (_dev(k, "k", k_cache.dtype, k_cache), _dev(v, "v", k_cache.dtype, k_cache),
+            _dev(slot_mapping, "slot_mapping", torch.int32, k_cache))
+    _lib.check(lib.pkv_store_kvcache(ctypes.byref(desc), *args, n, _stream(k_cache.device)))
+
+
+def paged_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                  cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor,
+                  block_tables: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int,
+                  scale: float, out: torch.Tensor | None = None) -> torch.Tensor:
+    """q [total_q, Hq, D] -> out [total_q, Hq, D]; sequences packed by cu_seqlens."""
+    lib = _lib.load()
+    desc = _cache_desc(k_cache, v_cache)
+    if q.dim() != 3 or q.shape[2] != k_cache.shape[3]:
+        raise ValueError("q must be [total_q, Hq, D]")
+    if block_tables.dim() != 2:
+        raise ValueError("block_tables must be [batch, stride]")
+    batch = cu_seqlens_q.numel() - 1
+    if cu_seqlens_k.numel() != batch + 1 or block_tables.shape[0] != batch:
+        raise ValueError("cu_seqlens_q, cu_seqlens_k and block_tables disagree on batch")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    args = (_dev(q, "q", k_cache.dtype, k_cache), _dev(out, "out", k_cache.dtype, k_cache),
+            q.shape[1], batch, _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32, k_cache),
+            _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32, k_cache), int(max_seqlen_q),
+            int(max_seqlen_k), _dev(block_tables, "block_tables", torch.int32, k_cache),
+            block_tables.shape[1], float(scale))
+    _lib.check(lib.pkv_paged_prefill(ctypes.byref(desc), *args, _stream(k_cache.device)))
+    return out
+
+
+def paged_decode_workspace_size(k_cache: torch.Tensor, v_cache: torch.Tensor, num_q_heads: int,
+                                batch: int, max_context_len: int, num_splits: int = 0) -> int:
+    desc = _cache_desc(k_cache, v_cache)
+    return int(_lib.load().pkv_paged_decode_workspace_size(
+        ctypes.byref(desc), num_q_heads, batch, max_context_len, num_splits))
+
+
+def paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                 block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
+                 scale: float, num_splits: int = 0, out: torch.Tensor | None = None,
+                 workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """q [B, Hq, D] -> out [B, Hq, D]; one query per sequence over its context."""
+    lib = _lib.load()
+    desc = _cache_desc(k_cache, v_cache)
+    if q.dim() != 3 or q.shape[2] != k_cache.shape[3]:
+        raise ValueError("q must be [B, Hq, D]")
+    batch = q.shape[0]
+    if context_lens.numel() != batch or block_tables.dim() != 2 or block_tables.shape[0] != batch:
+        raise ValueError("context_lens / block_tables disagree with q on batch")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    need = lib.pkv_paged_decode_workspace_size(ctypes.byref(desc), q.shape[1], batch,
+                                               int(max_context_len), int(num_splits))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    args = (_dev(q, "q", k_cache.dtype, k_cache), _dev(out, "out", k_cache.dtype, k_cache),
+            q.shape[1], batch, _dev(context_lens, "context_lens", torch.int32, k_cache),
+            int(max_context_len), _dev(block_tables, "block_tables", torch.int32, k_cache),
+            block_tables.shape[1], float(scale), ws_ptr, ws_bytes, int(num_splits))
+    _lib.check(lib.pkv_paged_decode(ctypes.byref(desc), *args, _stream(k_cache.device)))
+    return out

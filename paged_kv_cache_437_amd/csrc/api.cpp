@@ -1,0 +1,188 @@
+// C ABI of libpkv (declared in include/pkv.h): host-side validation and dispatch.
+// Nothing here touches the device before every host argument has been checked.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+
+#include "../../include/pkv.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+pkv_status fail(pkv_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+pkv_status ok() {
+  g_last_error[0] = '\0';
+  return PKV_OK;
+}
+
+int log2_exact(int x) {
+  int r = 0;
+  while ((1 << r) < x) ++r;
+  return (1 << r) == x ? r : -1;
+}
+
+pkv_status check_cache(const pkv_cache* c) {
+  if (c == nullptr) return fail(PKV_ERR_INVALID, "cache descriptor is NULL");
+  if (c->k_cache == nullptr || c->v_cache == nullptr)
+    return fail(PKV_ERR_INVALID, "k_cache / v_cache is NULL");
+  if (c->num_blocks <= 0 || c->num_kv_heads <= 0)
+    return fail(PKV_ERR_INVALID, "num_blocks and num_kv_heads must be positive");
+  if (c->dtype != PKV_F32 && c->dtype != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "dtype %d is not PKV_F32 or PKV_BF16", c->dtype);
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "head_dim %d (built: 64, 128)", c->head_dim);
+  if (c->block_size < 1 || c->block_size > 256 || log2_exact(c->block_size) < 0)
+    return fail(PKV_ERR_UNSUPPORTED, "block_size %d (built: powers of two in [1, 256])",
+                c->block_size);
+  return PKV_OK;
+}
+
+pkv_status check_heads(const pkv_cache* c, int32_t num_q_heads) {
+  if (num_q_heads <= 0 || num_q_heads % c->num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID, "num_q_heads %d is not a positive multiple of num_kv_heads %d",
+                num_q_heads, c->num_kv_heads);
+  if (num_q_heads > 65535) return fail(PKV_ERR_UNSUPPORTED, "num_q_heads %d > 65535", num_q_heads);
+  return PKV_OK;
+}
+
+pkv_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+size_t elem_size(const pkv_cache* c) { return c->dtype == PKV_F32 ? 4 : 2; }
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_status_string(pkv_status s) {
+  switch (s) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_INVALID: return "invalid argument";
+    case PKV_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case PKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case PKV_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+const char* pkv_last_error(void) { return g_last_error; }
+
+int32_t pkv_version(void) { return 100; }
+
+pkv_status pkv_store_kvcache(const pkv_cache* cache, const void* k, const void* v,
+                             const int32_t* slot_mapping, int32_t num_tokens,
+                             hipStream_t stream) {
+  pkv_status st = check_cache(cache);
+  if (st != PKV_OK) return st;
+  if (num_tokens < 0) return fail(PKV_ERR_INVALID, "num_tokens %d < 0", num_tokens);
+  if (num_tokens == 0) return ok();
+  if (k == nullptr || v == nullptr || slot_mapping == nullptr)
+    return fail(PKV_ERR_INVALID, "k, v or slot_mapping is NULL");
+  const size_t row_bytes = elem_size(cache) * cache->num_kv_heads * cache->head_dim;
+  if (row_bytes > (1u << 30)) return fail(PKV_ERR_UNSUPPORTED, "row of %zu bytes", row_bytes);
+  return launched(pkv::launch_store_kvcache(cache->k_cache, cache->v_cache, k, v, slot_mapping,
+                                            num_tokens, static_cast<int32_t>(row_bytes), stream),
+                  "store_kvcache");
+}
+
+pkv_status pkv_paged_prefill(const pkv_cache* cache, const void* q, void* out,
+                             int32_t num_q_heads, int32_t batch,
+                             const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                             int32_t max_seqlen_q, int32_t max_seqlen_k,
+                             const int32_t* block_tables, int32_t block_table_stride,
+                             float scale, hipStream_t stream) {
+  pkv_status st = check_cache(cache);
+  if (st != PKV_OK) return st;
+  if ((st = check_heads(cache, num_q_heads)) != PKV_OK) return st;
+  if (batch < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || block_table_stride < 0)
+    return fail(PKV_ERR_INVALID, "negative batch / max_seqlen / stride");
+  if (batch > 65535) return fail(PKV_ERR_UNSUPPORTED, "batch %d > 65535", batch);
+  if (batch == 0 || max_seqlen_q == 0) return ok();
+  if (q == nullptr || out == nullptr || cu_seqlens_q == nullptr || cu_seqlens_k == nullptr ||
+      block_tables == nullptr)
+    return fail(PKV_ERR_INVALID, "q, out, cu_seqlens_q/k or block_tables is NULL");
+  if (max_seqlen_k < max_seqlen_q)
+    return fail(PKV_ERR_INVALID, "max_seqlen_k %d < max_seqlen_q %d", max_seqlen_k, max_seqlen_q);
+  const int64_t need = (static_cast<int64_t>(max_seqlen_k) + cache->block_size - 1) /
+                       cache->block_size;
+  if (block_table_stride < need)
+    return fail(PKV_ERR_INVALID, "block_table_stride %d < ceil(max_seqlen_k / block_size) %lld",
+                block_table_stride, static_cast<long long>(need));
+  const int bs_log2 = log2_exact(cache->block_size);
+  return launched(pkv::launch_attention_generic(
+                      cache->dtype == PKV_BF16, cache->head_dim, q, out, cache->k_cache,
+                      cache->v_cache, num_q_heads, cache->num_kv_heads, bs_log2, batch,
+                      max_seqlen_q, cu_seqlens_q, cu_seqlens_k, nullptr, block_tables,
+                      block_table_stride, scale, stream),
+                  "paged_prefill");
+}
+
+size_t pkv_paged_decode_workspace_size(const pkv_cache* cache, int32_t num_q_heads,
+                                       int32_t batch, int32_t max_context_len,
+                                       int32_t num_splits) {
+  if (cache == nullptr || num_q_heads <= 0 || batch <= 0 || max_context_len <= 0 ||
+      num_splits < 0)
+    return 0;
+  if (cache->dtype != PKV_BF16) return 0;  // the fp32 path runs unsplit
+  int split_tokens = 0, max_splits = 0;
+  pkv::decode_split_plan(max_context_len, num_splits, &split_tokens, &max_splits);
+  if (max_splits <= 1) return 0;
+  const size_t n = static_cast<size_t>(batch) * num_q_heads * max_splits;
+  return n * static_cast<size_t>(cache->head_dim) * sizeof(float) + n * 2 * sizeof(float);
+}
+
+pkv_status pkv_paged_decode(const pkv_cache* cache, const void* q, void* out,
+                            int32_t num_q_heads, int32_t batch,
+                            const int32_t* context_lens, int32_t max_context_len,
+                            const int32_t* block_tables, int32_t block_table_stride,
+                            float scale, void* workspace, size_t workspace_bytes,
+                            int32_t num_splits, hipStream_t stream) {
+  pkv_status st = check_cache(cache);
+  if (st != PKV_OK) return st;
+  if ((st = check_heads(cache, num_q_heads)) != PKV_OK) return st;
+  if (batch < 0 || max_context_len < 0 || block_table_stride < 0 || num_splits < 0)
+    return fail(PKV_ERR_INVALID, "negative batch / max_context_len / stride / num_splits");
+  if (batch > 65535) return fail(PKV_ERR_UNSUPPORTED, "batch %d > 65535", batch);
+  if (batch == 0) return ok();
+  if (max_context_len == 0) return fail(PKV_ERR_INVALID, "max_context_len is 0");
+  if (q == nullptr || out == nullptr || context_lens == nullptr || block_tables == nullptr)
+    return fail(PKV_ERR_INVALID, "q, out, context_lens or block_tables is NULL");
+  const int64_t need = (static_cast<int64_t>(max_context_len) + cache->block_size - 1) /
+                       cache->block_size;
+  if (block_table_stride < need)
+    return fail(PKV_ERR_INVALID, "block_table_stride %d < ceil(max_context_len / block_size) %lld",
+                block_table_stride, static_cast<long long>(need));
+  const size_t ws = pkv_paged_decode_workspace_size(cache, num_q_heads, batch, max_context_len,
+                                                    num_splits);
+  if (ws > 0 && (workspace == nullptr || workspace_bytes < ws))
+    return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, ws);
+  const int bs_log2 = log2_exact(cache->block_size);
+  if (cache->dtype == PKV_BF16) {
+    int split_tokens = 0, max_splits = 0;
+    pkv::decode_split_plan(max_context_len, num_splits, &split_tokens, &max_splits);
+    return launched(pkv::launch_paged_decode_bf16(
+                        cache->head_dim, q, out, cache->k_cache, cache->v_cache, num_q_heads,
+                        cache->num_kv_heads, bs_log2, batch, context_lens, block_tables,
+                        block_table_stride, scale, split_tokens, max_splits, workspace, stream),
+                    "paged_decode");
+  }
+  return launched(pkv::launch_attention_generic(
+                      false, cache->head_dim, q, out, cache->k_cache, cache->v_cache,
+                      num_q_heads, cache->num_kv_heads, bs_log2, batch, 1, nullptr, nullptr,
+                      context_lens, block_tables, block_table_stride, scale, stream),
+                  "paged_decode");
+}
+
+}  // extern "C"

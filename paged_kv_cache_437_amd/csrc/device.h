@@ -1,0 +1,67 @@
+// Device-side helpers shared by the gfx950 kernels of libpkv.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// bf16 is the upper half of an IEEE binary32: widening is a shift.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// Element <-> float for the two storage types.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  typedef float storage;
+  static __device__ __forceinline__ float load(const float* p) { return *p; }
+  static __device__ __forceinline__ void store(float* p, float x) { *p = x; }
+};
+template <> struct Elem<uint16_t> {
+  typedef uint16_t storage;
+  static __device__ __forceinline__ float load(const uint16_t* p) {
+    return __uint_as_float(static_cast<uint32_t>(*p) << 16);
+  }
+  static __device__ __forceinline__ void store(uint16_t* p, float x) {
+    *p = static_cast<uint16_t>(f32_to_bf16_bits(x));
+  }
+};
+
+// Reductions over a full 64-lane wavefront (every lane gets the result).
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+// Row of token `pos` of a sequence for kv head `kvh`, as an element offset into a
+// [num_blocks][block_size][Hkv][D] cache.  64-bit: large pools exceed 2^31 elements.
+__device__ __forceinline__ int64_t token_row(int32_t block, int pos, int bs_log2, int Hkv,
+                                             int kvh, int D) {
+  const int64_t slot = (static_cast<int64_t>(block) << bs_log2) | (pos & ((1 << bs_log2) - 1));
+  return (slot * Hkv + kvh) * D;
+}
+
+}  // namespace pkv

@@ -1,0 +1,40 @@
+// Host-side launchers of the libpkv kernels (internal; the public API is include/pkv.h).
+// Every launcher enqueues on `stream` and returns hipGetLastError() of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+// Row copy through a slot mapping; row_bytes = Hkv * D * element size (multiple of 16).
+hipError_t launch_store_kvcache(void* k_cache, void* v_cache, const void* k, const void* v,
+                                const int32_t* slot_mapping, int32_t num_tokens,
+                                int32_t row_bytes, hipStream_t stream);
+
+// Generic attention: one wavefront per (query row, q head), vector ALU only.  Serves
+// fp32 prefill and decode.  Decode when `context_lens` is non-null (one query per
+// sequence), otherwise packed prefill over cu_seqlens_q / cu_seqlens_k.
+hipError_t launch_attention_generic(bool bf16, int head_dim, const void* q, void* out,
+                                    const void* k_cache, const void* v_cache, int num_q_heads,
+                                    int num_kv_heads, int bs_log2, int batch, int max_q_rows,
+                                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                    const int32_t* context_lens, const int32_t* block_tables,
+                                    int table_stride, float scale, hipStream_t stream);
+
+// Split plan of the bf16 decode: splits of `split_tokens` tokens (a multiple of 256),
+// at most `max_splits` per sequence.  num_splits == 0 picks 256-token splits.
+void decode_split_plan(int max_context_len, int num_splits, int* split_tokens, int* max_splits);
+
+// bf16 paged decode: split kernel (+ combine kernel when max_splits > 1).  The
+// workspace holds [batch][Hq][max_splits][head_dim] float partial outputs followed by
+// [batch][Hq][max_splits] float2 (max, sum) pairs; unused when max_splits == 1.
+hipError_t launch_paged_decode_bf16(int head_dim, const void* q, void* out, const void* k_cache,
+                                    const void* v_cache, int num_q_heads, int num_kv_heads,
+                                    int bs_log2, int batch, const int32_t* context_lens,
+                                    const int32_t* block_tables, int table_stride, float scale,
+                                    int split_tokens, int max_splits, void* workspace,
+                                    hipStream_t stream);
+
+}  // namespace pkv

@@ -1,0 +1,77 @@
+"""Control plane (row a1): the product's vectorised planner against the oracle's
+plain BlockManager, bit for bit, plus pool invariants.  No GPU."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from oracle_pins import tiny_workloads
+from paged_kv_cache_437_amd.control import BlockPool, plan_step
+
+
+def _compare(wl):
+    ref = oracle.plan_step(wl)
+    pool = BlockPool(wl.num_blocks, wl.free_order)
+    got = plan_step(wl.seqs, wl.block_size, pool)
+    assert [t.tolist() for t in got.tables] == ref["tables"]
+    for part, seq, pos, slots in (("history_slots", got.history_seq, got.history_pos,
+                                   got.history_slots),
+                                  ("step_slots", got.step_seq, got.step_pos, got.step_slots)):
+        want = np.array(ref[part], np.int64).reshape(-1, 3)
+        assert np.array_equal(seq, want[:, 0]), part
+        assert np.array_equal(pos, want[:, 1]), part
+        assert np.array_equal(slots.astype(np.int64), want[:, 2]), part
+        assert slots.dtype == np.int32
+    assert got.prefill == ref["prefill"] and got.decode == ref["decode"]
+    assert got.cu_seqlens_q.tolist() == ref["cu_seqlens_q"]
+    assert got.cu_seqlens_k.tolist() == ref["cu_seqlens_k"]
+    assert got.context_lens.tolist() == ref["context_lens"]
+    assert got.prefill_block_tables.tolist() == ref["prefill_block_tables"]
+    assert got.decode_block_tables.tolist() == ref["decode_block_tables"]
+    used = {b: int(pool.ref[b]) for b in range(wl.num_blocks) if pool.ref[b] > 0}
+    assert used == ref["ref_counts"]
+
+
+@pytest.mark.parametrize("name", workloads.CONFIG_NAMES)
+def test_configs_match_oracle_planner(name):
+    _compare(workloads.by_name(name, seed=0, with_values=False))
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_tiny_workloads_match_oracle_planner(seed):
+    for wl in tiny_workloads(seed):
+        _compare(wl)
+
+
+def test_prefix_blocks_shared_with_ref_counts():
+    wl = workloads.prefill_prefix_cached(0, with_values=False)
+    pool = BlockPool(wl.num_blocks, wl.free_order)
+    plan = plan_step(wl.seqs, wl.block_size, pool)
+    prefix = plan.tables[0][:4]
+    assert all(np.array_equal(t[:4], prefix) for t in plan.tables)
+    assert all(pool.ref[b] == 64 for b in prefix)
+    assert len({int(t[4]) for t in plan.tables}) == 64
+    assert len(plan.history_slots) == 1024  # the prefix is written once
+    assert pool.num_free == wl.num_blocks - 68
+
+
+def test_pool_exhaustion_and_release_order():
+    pool = BlockPool(4, [2, 0, 3, 1])
+    assert [pool.allocate() for _ in range(4)] == [2, 0, 3, 1]
+    assert pool.allocate() is None and pool.allocate_many(1) is None
+    pool.share(0)
+    pool.release(0)
+    assert pool.num_free == 0
+    pool.release(3)
+    pool.release(0)
+    assert [pool.allocate(), pool.allocate(), pool.allocate()] == [3, 0, None]
+    with pytest.raises(ValueError):
+        pool.release(2) or pool.release(2)
+
+
+def test_planner_raises_on_exhaustion():
+    wl = workloads.custom("small_pool", "f32", 2, 1, 64, 16, [workloads.SeqSpec("decode", 40, 1)],
+                          pool_blocks=3)
+    pool = BlockPool(2, [1, 0])
+    with pytest.raises(MemoryError):
+        plan_step(wl.seqs, wl.block_size, pool)

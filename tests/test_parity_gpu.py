@@ -1,0 +1,176 @@
+"""HIP path vs the CPU oracle on the same seeded inputs, through the C ABI.
+
+Sizes: every config at its full size (the oracle finishes them in seconds; the
+large decode batch is checked on sampled sequences with the oracle run one
+sequence at a time), plus edge cases.  Criteria: KV writes and one-hot index
+probes bit-exact; fp32 max |err| <= 1e-5; bf16 max |err| <= 2e-2 and mean
+|err| <= 2e-3.  Invariances (relabelled blocks, shared vs copied prefix, stale
+poison, reruns) must hold bit for bit on the GPU.
+"""
+from __future__ import annotations
+
+import copy
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from oracle_pins import one_hot_probe
+from parity_util import assert_close, edge_workloads
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pkv():
+    import paged_kv_cache_437_amd as pkv
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    pkv._lib.load()
+    return pkv
+
+
+def _step(wl, **kw):
+    from paged_kv_cache_437_amd.step import DeviceStep
+    return DeviceStep(wl, device="cuda", **kw).run()
+
+
+def _check_outputs(wl, st, ref):
+    got = st.outputs_numpy()
+    torch.cuda.synchronize()
+    for key in ("prefill", "decode"):
+        if key in ref:
+            assert_close(got[key], ref[key], wl.dtype, f"{wl.name} {key}")
+
+
+def _cache_bits(t):
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.view(torch.int32).cpu().numpy().view(np.uint32)
+
+
+@pytest.mark.parametrize("name", ["tiny_mixed", "decode_mha", "prefill_varlen",
+                                  "prefill_prefix_cached"])
+def test_config_parity(pkv, name):
+    wl = workloads.by_name(name, seed=0)
+    st = _step(wl)
+    ref = oracle.run_step(wl)
+    # KV write: the whole pool, bit for bit (written rows and untouched stale rows)
+    for dev, host in ((st.k_cache, ref["k_cache"]), (st.v_cache, ref["v_cache"])):
+        bits = _cache_bits(dev)
+        want = host.view(np.uint32) if host.dtype == np.float32 else host
+        assert np.array_equal(bits, want), f"{name}: cache differs from the oracle's writes"
+    _check_outputs(wl, st, ref)
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_config_parity_more_seeds(pkv, seed):
+    for name in ("tiny_mixed", "prefill_varlen"):
+        wl = workloads.by_name(name, seed=seed)
+        _check_outputs(wl, _step(wl), oracle.run_step(wl))
+
+
+def test_decode_large_full_size_sampled(pkv):
+    """Large decode batch with the pool at 60% of free device memory, in the
+    launch configuration the bench times (automatic splits); 64 sequences
+    spanning the length range are checked against the oracle one by one."""
+    free, _ = torch.cuda.mem_get_info()
+    bb = workloads.block_bytes(256, 8, 128, 2)
+    wl = workloads.decode_large(seed=0, pool_blocks=int(0.6 * free // bb))
+    st = _step(wl)
+    got = st.outputs_numpy()["decode"]
+    lens = np.array([s.context_len for s in wl.seqs])
+    order = np.argsort(lens, kind="stable")
+    picks = sorted(set(order[::4].tolist()) | {int(order[0]), int(order[-1])})
+    want = np.stack([oracle.causal_attention(wl.q[i], wl.k[i], wl.v[i], wl.scale)[0]
+                     for i in picks])
+    assert_close(got[picks], want, "bf16", "decode_large sampled")
+    del st
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("idx", range(8))
+def test_edge_cases(pkv, idx):
+    wl = edge_workloads(seed=10)[idx]
+    _check_outputs(wl, _step(wl), oracle.run_step(wl))
+
+
+def test_one_hot_probes_bit_exact(pkv):
+    S = workloads.SeqSpec
+    seqs = [S("decode", 530, 1)] * 6 + [S("prefill", 530, 3)]
+    wl = workloads.custom("probe", "bf16", 8, 2, 128, 16, seqs, seed=5, scale=0.25)
+    targets = [0, 15, 16, 255, 256, 529, 529]  # block edges, and the newest key
+    for i, t in enumerate(targets):
+        one_hot_probe(wl, i, t)
+    st = _step(wl)
+    got = st.outputs_numpy()
+    ref = oracle.run_step(wl)
+    assert np.array_equal(got["decode"], ref["decode"]), "decode probe not bit-exact"
+    assert np.array_equal(got["prefill"][2], ref["prefill"][2]), "prefill probe not bit-exact"
+    for i in range(6):
+        v = oracle.bf16_bits_to_float(wl.v[i][targets[i]])
+        assert np.array_equal(got["decode"][i], np.repeat(v, 4, axis=0))
+
+
+def _bits(st):
+    return {k: v.copy() for k, v in st.outputs_numpy().items()}
+
+
+def test_relabel_invariance_bit_identical(pkv):
+    for wl in (workloads.prefill_varlen(3), workloads.decode_mha(3), edge_workloads(3)[0]):
+        a = _bits(_step(wl))
+        wl2 = copy.copy(wl)
+        wl2.num_blocks = wl.num_blocks + 7
+        wl2.free_order = np.random.default_rng(77).permutation(wl2.num_blocks)
+        b = _bits(_step(wl2))
+        for k in a:
+            assert np.array_equal(a[k], b[k]), f"{wl.name}: block relabelling changed {k}"
+
+
+def test_prefix_shared_vs_copied_bit_identical(pkv):
+    wl = workloads.prefill_prefix_cached(seed=4, batch=8)
+    shared = _bits(_step(wl))
+    wl2 = copy.copy(wl)
+    wl2.seqs = [workloads.SeqSpec(s.phase, s.context_len, s.new_tokens) for s in wl.seqs]
+    wl2.num_blocks = 8 * 5 + 3
+    wl2.free_order = np.arange(wl2.num_blocks)[::-1].copy()
+    private = _bits(_step(wl2))
+    assert np.array_equal(shared["prefill"], private["prefill"])
+
+
+def test_stale_poison_bit_identical(pkv):
+    for wl in (edge_workloads(5)[0], edge_workloads(5)[2], workloads.prefill_varlen(5)):
+        outs = [_bits(_step(wl, stale=s)) for s in ("nan", "inf", "-inf", "huge")]
+        for k in outs[0]:
+            assert np.isfinite(outs[0][k]).all(), f"{wl.name}: stale value leaked into {k}"
+            for o in outs[1:]:
+                assert np.array_equal(outs[0][k], o[k]), f"{wl.name}: stale contents leaked"
+
+
+def test_rerun_deterministic(pkv):
+    wl = workloads.decode_mha(6)
+    st = _step(wl)
+    a = _bits(st)
+    st.run()
+    b = _bits(st)
+    assert np.array_equal(a["decode"], b["decode"])
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 7])
+def test_split_count_agrees(pkv, splits):
+    wl = workloads.decode_large(seed=8, batch=24)
+    ref = oracle.run_step(wl)
+    _check_outputs(wl, _step(wl, num_splits=splits), ref)
+
+
+def test_decode_equals_last_prefill_row(pkv):
+    L = 1000
+    S = workloads.SeqSpec
+    wl = workloads.custom("dec_vs_pre", "bf16", 16, 8, 128, 256, [S("prefill", L, L),
+                                                                    S("decode", L, 1)], seed=9)
+    wl.k[1], wl.v[1] = wl.k[0].copy(), wl.v[0].copy()
+    wl.q[1] = wl.q[0][-1:].copy()
+    got = _step(wl).outputs_numpy()
+    assert_close(got["decode"][0], got["prefill"][L - 1], "bf16", "decode vs last prefill row")

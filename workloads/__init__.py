@@ -14,16 +14,21 @@ spans several blocks; sequences sharing a prefix share ref-counted block ids;
 prefill packs a batch of sequences by cumulative lengths and decode adds one
 token per sequence.
 
-Draw order for every workload (one ``numpy.random.default_rng(seed)``):
-lengths -> permutation of pool ids (the free list's initial order) -> Q -> K -> V.
-K and V are drawn over the unique tokens in sequence order (a shared prefix is
-drawn once, before the per-sequence tokens).  Values are N(0, 1) in float32;
-bf16 workloads round them to bf16 with round-to-nearest-even and both sides
-receive the same bf16 bit patterns (uint16 arrays).
+Draw order for every workload (``numpy.random.default_rng(seed)``): lengths ->
+permutation of pool ids (the free list's initial order) -> four 32-bit words that
+seed the value streams.  Q, K and V then come from three child seed sequences of
+those words, each split into fixed chunks of 8192 rows with one child stream per
+chunk (deterministic, and drawn in parallel).  K and V are drawn over the unique
+tokens in sequence order (a shared prefix is drawn once, before the
+per-sequence tokens).  Values are N(0, 1) in float32; bf16 workloads round them
+to bf16 with round-to-nearest-even and both sides receive the same bf16 bit
+patterns (uint16 arrays).
 """
 from __future__ import annotations
 
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -121,20 +126,42 @@ def block_bytes(block_size: int, num_kv_heads: int, head_dim: int, elem_bytes: i
     return 2 * block_size * num_kv_heads * head_dim * elem_bytes
 
 
-def _values(rng, n_rows, heads, dim, dtype, chunk_rows=1 << 15):
-    """Draw [n_rows, heads, dim] N(0,1) float32 values (bf16 bits when dtype == 'bf16')."""
+_CHUNK_ROWS = 8192
+
+
+def _values(seed_seq, n_rows, heads, dim, dtype):
+    """Draw [n_rows, heads, dim] N(0,1) float32 values (bf16 bits when dtype == 'bf16').
+
+    Rows come in fixed chunks of 8192; chunk c is drawn by the c-th child of
+    ``seed_seq``, so the values depend on the seed only (not on how many threads
+    draw them) and large workloads are generated in parallel."""
     out_dtype = np.float32 if dtype == "f32" else np.uint16
     out = np.empty((n_rows, heads, dim), out_dtype)
-    for r0 in range(0, n_rows, chunk_rows):
-        r1 = min(n_rows, r0 + chunk_rows)
-        x = rng.standard_normal((r1 - r0, heads, dim), dtype=np.float32)
+    n_chunks = -(-n_rows // _CHUNK_ROWS)
+    children = seed_seq.spawn(n_chunks)
+
+    def draw(c):
+        r0 = c * _CHUNK_ROWS
+        r1 = min(n_rows, r0 + _CHUNK_ROWS)
+        x = np.random.default_rng(children[c]).standard_normal((r1 - r0, heads, dim),
+                                                                dtype=np.float32)
         out[r0:r1] = x if dtype == "f32" else round_to_bf16_bits(x)
+
+    if n_chunks <= 2:
+        for c in range(n_chunks):
+            draw(c)
+    else:
+        workers = max(1, min(16, len(os.sched_getaffinity(0))))
+        with ThreadPoolExecutor(workers) as ex:
+            list(ex.map(draw, range(n_chunks)))
     return out
 
 
 def _finish(name, dtype, hq, hkv, d, bs, seqs, rng, seed, pool_blocks=None, pool_scale=1.25,
-            scale=None):
-    """Permutation of pool ids, then Q, K, V draws (in that order)."""
+            scale=None, with_values=True):
+    """Permutation of pool ids, then Q, K, V draws (in that order).  With
+    ``with_values=False`` only shapes, pool and free-list order are drawn (the
+    values, drawn last, would not change them)."""
     wl = Workload(name=name, dtype=dtype, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
                   block_size=bs, num_blocks=0, free_order=np.empty(0, np.int64),
                   scale=(1.0 / math.sqrt(d)) if scale is None else scale, seed=seed, seqs=seqs)
@@ -145,9 +172,13 @@ def _finish(name, dtype, hq, hkv, d, bs, seqs, rng, seed, pool_blocks=None, pool
         raise ValueError(f"pool of {pool_blocks} blocks cannot hold {used} used blocks")
     wl.num_blocks = int(pool_blocks)
     wl.free_order = rng.permutation(wl.num_blocks).astype(np.int64)
+    if not with_values:
+        return wl
 
+    q_seq, k_seq, v_seq = np.random.SeedSequence(
+        [int(x) for x in rng.integers(0, 2**32, size=4, dtype=np.uint64)]).spawn(3)
     total_q = sum(s.new_tokens for s in seqs)
-    q_all = _values(rng, total_q, hq, d, dtype)
+    q_all = _values(q_seq, total_q, hq, d, dtype)
     # unique K/V tokens: each shared prefix once, then every sequence's own tokens
     groups = {}
     for s in seqs:
@@ -157,8 +188,8 @@ def _finish(name, dtype, hq, hkv, d, bs, seqs, rng, seed, pool_blocks=None, pool
     for s in seqs:
         own_len.append(s.context_len - (s.prefix_len if s.prefix_group >= 0 else 0))
     n_unique = sum(groups.values()) + sum(own_len)
-    k_all = _values(rng, n_unique, hkv, d, dtype)
-    v_all = _values(rng, n_unique, hkv, d, dtype)
+    k_all = _values(k_seq, n_unique, hkv, d, dtype)
+    v_all = _values(v_seq, n_unique, hkv, d, dtype)
 
     prefix_rows = {}
     off = 0
@@ -182,48 +213,55 @@ def _finish(name, dtype, hq, hkv, d, bs, seqs, rng, seed, pool_blocks=None, pool
     return wl
 
 
-def tiny_mixed(seed: int = 0) -> Workload:
+def tiny_mixed(seed: int = 0, with_values: bool = True) -> Workload:
     """Tiny fp32 mixed step: 2 q heads / 1 kv head, head_dim 64, block_size 16,
     pool 32 blocks; prefill of two prompts (5 and 33 tokens) and decode of two
     sequences (contexts 17 and 64, the new token included); scale 1/sqrt(64)."""
     rng = np.random.default_rng(seed)
     seqs = [SeqSpec("prefill", 5, 5), SeqSpec("prefill", 33, 33),
             SeqSpec("decode", 17, 1), SeqSpec("decode", 64, 1)]
-    return _finish("tiny_mixed_fp32", "f32", 2, 1, 64, 16, seqs, rng, seed, pool_blocks=32)
+    return _finish("tiny_mixed_fp32", "f32", 2, 1, 64, 16, seqs, rng, seed, pool_blocks=32,
+                   with_values=with_values)
 
 
-def decode_mha(seed: int = 0, batch: int = 32, lo: int = 512, hi: int = 4096) -> Workload:
+def decode_mha(seed: int = 0, batch: int = 32, lo: int = 512, hi: int = 4096,
+               with_values: bool = True) -> Workload:
     """Decode step of a 7B-shaped layer: 32 q / 32 kv heads, head_dim 128, block_size 256,
     32 sequences with context lengths uniform on [512, 4096] (inclusive integers),
     pool 1.25x the used blocks, one new token per sequence."""
     rng = np.random.default_rng(seed)
     lens = rng.integers(lo, hi, size=batch, endpoint=True)
     seqs = [SeqSpec("decode", int(L), 1) for L in lens]
-    return _finish("decode_mha_bf16", "bf16", 32, 32, 128, 256, seqs, rng, seed)
+    return _finish("decode_mha_bf16", "bf16", 32, 32, 128, 256, seqs, rng, seed,
+                   with_values=with_values)
 
 
-def prefill_varlen(seed: int = 0, batch: int = 16, lo: int = 128, hi: int = 2048) -> Workload:
+def prefill_varlen(seed: int = 0, batch: int = 16, lo: int = 128, hi: int = 2048,
+                   with_values: bool = True) -> Workload:
     """Varlen causal prefill, GQA 16 q / 8 kv heads, head_dim 128, block_size 256,
     16 prompts with lengths uniform on [128, 2048]; every token is new."""
     rng = np.random.default_rng(seed)
     lens = rng.integers(lo, hi, size=batch, endpoint=True)
     seqs = [SeqSpec("prefill", int(L), int(L)) for L in lens]
-    return _finish("prefill_varlen_bf16", "bf16", 16, 8, 128, 256, seqs, rng, seed)
+    return _finish("prefill_varlen_bf16", "bf16", 16, 8, 128, 256, seqs, rng, seed,
+                   with_values=with_values)
 
 
 def prefill_prefix_cached(seed: int = 0, batch: int = 64, prefix: int = 1024,
-                          suffix: int = 256) -> Workload:
+                          suffix: int = 256, with_values: bool = True) -> Workload:
     """Prefix-cached prefill: 32 q / 8 kv heads, head_dim 128, block_size 256; 64
     sequences share a 1024-token prefix (4 blocks, written once before the step)
     and each has a 256-token suffix; only suffix tokens are queries."""
     rng = np.random.default_rng(seed)
     seqs = [SeqSpec("prefill", prefix + suffix, suffix, prefix_group=0, prefix_len=prefix)
             for _ in range(batch)]
-    return _finish("prefill_prefix_cached_bf16", "bf16", 32, 8, 128, 256, seqs, rng, seed)
+    return _finish("prefill_prefix_cached_bf16", "bf16", 32, 8, 128, 256, seqs, rng, seed,
+                   with_values=with_values)
 
 
 def decode_large(seed: int = 0, batch: int = 256, pool_blocks: int | None = None,
-                 median: int = 2048, lo: int = 64, hi: int = 16384) -> Workload:
+                 median: int = 2048, lo: int = 64, hi: int = 16384,
+                 with_values: bool = True) -> Workload:
     """Large decode batch, GQA 32 q / 8 kv heads, head_dim 128, block_size 256;
     256 sequences with ln(context) ~ N(ln 2048, 1), rounded and clipped to
     [64, 16384].  ``pool_blocks`` is the pool size (the caller derives it from
@@ -232,7 +270,7 @@ def decode_large(seed: int = 0, batch: int = 256, pool_blocks: int | None = None
     lens = np.clip(np.rint(np.exp(rng.normal(math.log(median), 1.0, size=batch))), lo, hi)
     seqs = [SeqSpec("decode", int(L), 1) for L in lens.astype(np.int64)]
     return _finish("decode_large_bf16", "bf16", 32, 8, 128, 256, seqs, rng, seed,
-                   pool_blocks=pool_blocks)
+                   pool_blocks=pool_blocks, with_values=with_values)
 
 
 def custom(name, dtype, hq, hkv, d, bs, seqs, seed=0, pool_blocks=None, scale=None) -> Workload:
