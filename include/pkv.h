@@ -94,7 +94,8 @@ pkv_status pkv_store_kvcache(const pkv_cache* cache, const void* k, const void* 
  *   max_seqlen_k   host upper bound on every Lk
  *   block_tables   [batch][block_table_stride] int32; only entries
  *                  0 .. ceil(Lk / block_size)-1 of a row are read
- *   scale          multiplies q.k before the softmax (usually 1/sqrt(head_dim))
+ *   scale          multiplies q.k before the softmax (usually 1/sqrt(head_dim));
+ *                  must be finite and > 0 (PKV_ERR_INVALID otherwise)
  * Contract: Lk >= Lq, Lk >= 1 when Lq > 0, ceil(Lk/block_size) <=
  * block_table_stride, used table entries in [0, num_blocks).  Rows of out
  * outside [0, total_q) are not written. */

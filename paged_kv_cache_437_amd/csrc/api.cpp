@@ -2,6 +2,7 @@
 // Nothing here touches the device before every host argument has been checked.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 
@@ -120,12 +121,20 @@ pkv_status pkv_paged_prefill(const pkv_cache* cache, const void* q, void* out,
   if (block_table_stride < need)
     return fail(PKV_ERR_INVALID, "block_table_stride %d < ceil(max_seqlen_k / block_size) %lld",
                 block_table_stride, static_cast<long long>(need));
+  if (!(scale > 0.f) || !std::isfinite(scale))
+    return fail(PKV_ERR_INVALID, "scale %g must be finite and positive", scale);
   const int bs_log2 = log2_exact(cache->block_size);
+  if (cache->dtype == PKV_BF16)
+    return launched(pkv::launch_paged_prefill_bf16(
+                        cache->head_dim, q, out, cache->k_cache, cache->v_cache, num_q_heads,
+                        cache->num_kv_heads, bs_log2, batch, max_seqlen_q, cu_seqlens_q,
+                        cu_seqlens_k, block_tables, block_table_stride, scale, stream),
+                    "paged_prefill");
   return launched(pkv::launch_attention_generic(
-                      cache->dtype == PKV_BF16, cache->head_dim, q, out, cache->k_cache,
-                      cache->v_cache, num_q_heads, cache->num_kv_heads, bs_log2, batch,
-                      max_seqlen_q, cu_seqlens_q, cu_seqlens_k, nullptr, block_tables,
-                      block_table_stride, scale, stream),
+                      false, cache->head_dim, q, out, cache->k_cache, cache->v_cache,
+                      num_q_heads, cache->num_kv_heads, bs_log2, batch, max_seqlen_q,
+                      cu_seqlens_q, cu_seqlens_k, nullptr, block_tables, block_table_stride,
+                      scale, stream),
                   "paged_prefill");
 }
 
@@ -164,6 +173,8 @@ pkv_status pkv_paged_decode(const pkv_cache* cache, const void* q, void* out,
   if (block_table_stride < need)
     return fail(PKV_ERR_INVALID, "block_table_stride %d < ceil(max_context_len / block_size) %lld",
                 block_table_stride, static_cast<long long>(need));
+  if (!(scale > 0.f) || !std::isfinite(scale))
+    return fail(PKV_ERR_INVALID, "scale %g must be finite and positive", scale);
   const size_t ws = pkv_paged_decode_workspace_size(cache, num_q_heads, batch, max_context_len,
                                                     num_splits);
   if (ws > 0 && (workspace == nullptr || workspace_bytes < ws))

@@ -37,4 +37,12 @@ hipError_t launch_paged_decode_bf16(int head_dim, const void* q, void* out, cons
                                     int split_tokens, int max_splits, void* workspace,
                                     hipStream_t stream);
 
+// bf16 varlen causal prefill on MFMA (one launch).
+hipError_t launch_paged_prefill_bf16(int head_dim, const void* q, void* out, const void* k_cache,
+                                     const void* v_cache, int num_q_heads, int num_kv_heads,
+                                     int bs_log2, int batch, int max_seqlen_q,
+                                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                     const int32_t* block_tables, int table_stride, float scale,
+                                     hipStream_t stream);
+
 }  // namespace pkv

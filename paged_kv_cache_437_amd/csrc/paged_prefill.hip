@@ -1,0 +1,326 @@
+// Paged varlen causal prefill, bf16 in / fp32 accumulate, on gfx950 MFMA.
+//
+// What is computed (nano-vLLM pages, lnwmold article, "Preparing for computation":
+// prefill packs sequences and addresses them by cumulative lengths; "Prefix Caching
+// by hashing": a cached prefix is read from its shared blocks, not recomputed):
+// sequence b owns query rows cu_q[b] .. cu_q[b+1]-1 (Lq of them) and Lk keys read
+// through block_tables[b]; query i sits at position Lk - Lq + i and
+//   out = softmax_j(scale * q . k_j) v_j   over keys j <= Lk - Lq + i.
+//
+// Tiling.  A workgroup (4 wavefronts) owns 128 query rows = all the q heads of one
+// kv head over a tile of 128/GP tokens (GP = q heads per kv head rounded up to a
+// power of two), so every K/V tile staged in LDS serves all grouped heads.  Each
+// wave owns 32 rows (one head, consecutive tokens when GP <= 4).  Per 64-key tile:
+//   S^T (keys x rows) = K Q^T    with v_mfma_f32_32x32x16_bf16, A = K rows from LDS
+//                                (16-byte reads), B = the wave's q rows held in VGPRs;
+//   online softmax in the log2 domain: each lane owns one query row (16 of the 32
+//                                keys of each 32-key block; the other 16 are in lane
+//                                l^32), so a row max is a local max plus one swap;
+//   O^T (d x rows) += V^T P^T    A = V^T built with ds_read_tr16_b64 from the
+//                                row-major V tile, B = P converted to bf16 in place.
+// The key order inside each MFMA k-step is the same permutation for both operands,
+// so the P registers produced by the S^T MFMA feed the O^T MFMA without shuffles.
+// K/V tiles are double buffered in LDS with rows padded to (D + 16) elements (no
+// bank conflicts for the 16-byte and the transposing reads); tile j+1 is fetched
+// into registers while tile j is computed.  Keys at or past Lk are zero-filled
+// (stale rows never enter), table entries past the last used block are never read,
+// and causal masking is applied only on tiles that cross the diagonal.
+// Work order: blockIdx.x = (sequence, kv head), blockIdx.y = tile rank counted from
+// each sequence's last (heaviest) tile, so long causal tiles start first and the
+// tiles sharing one sequence's K/V land on the same XCD when Hkv * batch % 8 == 0.
+#include "device.h"
+#include "launch.h"
+#include "timing.h"
+
+namespace pkv {
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ i16x4_t lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4_t*)(
+          reinterpret_cast<__attribute__((address_space(3))) uint16_t*>(
+              reinterpret_cast<uintptr_t>(p))));
+}
+
+template <int D, int GP>
+__global__ __launch_bounds__(256, 2) void paged_prefill_bf16_kernel(
+    const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
+    const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
+    const int32_t* __restrict__ cu_seqlens_q, const int32_t* __restrict__ cu_seqlens_k,
+    const int32_t* __restrict__ block_tables, int table_stride, int Hq, int Hkv, int G,
+    int bs_log2, float scale_log2) {
+  static_assert(D == 64 || D == 128, "head_dim");
+  constexpr int BM_TOK = 128 / GP;  // tokens per workgroup tile
+  constexpr int BN = 64;            // keys per K/V tile
+  constexpr int KP = D + 16;        // padded LDS row (elements)
+  constexpr int KS = D / 16;        // S^T MFMA k-steps over head_dim
+  constexpr int DT = D / 32;        // O^T tiles of 32 head_dim rows
+  constexpr int CPR = D / 8;        // 16-byte chunks per K/V row
+  constexpr int RPI = 256 / CPR;    // rows per workgroup load instruction
+  constexpr int LIT = BN / RPI;     // load instructions per tile (K and V each)
+
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][BN][KP];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][BN][KP];
+
+  const int b = blockIdx.x / Hkv;
+  const int kvh = blockIdx.x - b * Hkv;
+  const int q_begin = cu_seqlens_q[b];
+  const int Lq = cu_seqlens_q[b + 1] - q_begin;
+  const int Lk = cu_seqlens_k[b + 1] - cu_seqlens_k[b];
+  const int n_tiles = (Lq + BM_TOK - 1) / BM_TOK;
+  const int tile = n_tiles - 1 - static_cast<int>(blockIdx.y);
+  if (tile < 0) return;  // uniform, before any barrier
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  const int tok0 = tile * BM_TOK;
+  const int32_t* table = block_tables + static_cast<int64_t>(b) * table_stride;
+  const int bs_mask = (1 << bs_log2) - 1;
+
+  // this lane's query row (rows are head-major: 32 rows of a wave share a head when GP<=4)
+  const int R = 32 * wave + l32;
+  const int head = R / BM_TOK;
+  const int tok = tok0 + (R - head * BM_TOK);
+  const bool row_valid = head < G && tok < Lq;
+  const int hq = kvh * G + head;
+  const int diag = Lk - Lq + tok;  // last visible key of this row (any value is fine if invalid)
+
+  // q row as the S^T MFMA B operand: lane holds d = ks*16 + 8*hi .. +8
+  bf16x8_t qb[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    u32x4_t w = {0u, 0u, 0u, 0u};
+    if (row_valid)
+      w = *reinterpret_cast<const u32x4_t*>(
+          q + (static_cast<int64_t>(q_begin + tok) * Hq + hq) * D + ks * 16 + 8 * hi);
+    qb[ks] = __builtin_bit_cast(bf16x8_t, w);
+  }
+
+  // keys the workgroup needs: up to the diagonal of its last valid token
+  const int tok_last = min(tok0 + BM_TOK, Lq) - 1;
+  const int k_end = Lk - Lq + tok_last + 1;
+  const int n_kv = (k_end + BN - 1) / BN;
+  const int first_masked_tile = (Lk - Lq + tok0) / BN;  // tiles before it need no mask
+
+  // global -> register staging of one K/V tile
+  const int ld_row = tid / CPR;
+  const int ld_chunk = tid - ld_row * CPR;
+  u32x4_t kst[LIT], vst[LIT];
+  auto fetch = [&](int t) {
+    const int kv0 = t * BN;
+    if (bs_log2 >= 6) {
+      const int64_t blk = table[kv0 >> bs_log2];
+#pragma unroll
+      for (int it = 0; it < LIT; ++it) {
+        const int key = kv0 + it * RPI + ld_row;
+        u32x4_t kw = {0u, 0u, 0u, 0u}, vw = {0u, 0u, 0u, 0u};
+        if (key < Lk) {
+          const int64_t off =
+              (((blk << bs_log2) | (key & bs_mask)) * Hkv + kvh) * D + ld_chunk * 8;
+          kw = *reinterpret_cast<const u32x4_t*>(k_cache + off);
+          vw = *reinterpret_cast<const u32x4_t*>(v_cache + off);
+        }
+        kst[it] = kw;
+        vst[it] = vw;
+      }
+    } else {
+#pragma unroll
+      for (int it = 0; it < LIT; ++it) {
+        const int key = kv0 + it * RPI + ld_row;
+        u32x4_t kw = {0u, 0u, 0u, 0u}, vw = {0u, 0u, 0u, 0u};
+        if (key < Lk) {
+          const int64_t off =
+              token_row(table[key >> bs_log2], key, bs_log2, Hkv, kvh, D) + ld_chunk * 8;
+          kw = *reinterpret_cast<const u32x4_t*>(k_cache + off);
+          vw = *reinterpret_cast<const u32x4_t*>(v_cache + off);
+        }
+        kst[it] = kw;
+        vst[it] = vw;
+      }
+    }
+  };
+  auto stage = [&](int buf) {
+#pragma unroll
+    for (int it = 0; it < LIT; ++it) {
+      *reinterpret_cast<u32x4_t*>(&k_lds[buf][it * RPI + ld_row][ld_chunk * 8]) = kst[it];
+      *reinterpret_cast<u32x4_t*>(&v_lds[buf][it * RPI + ld_row][ld_chunk * 8]) = vst[it];
+    }
+  };
+
+  f32x16_t o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+  float m = -INFINITY;  // running max of raw scores of this row
+  float l = 0.f;        // this lane's share of the running sum
+
+  fetch(0);
+  stage(0);
+  __syncthreads();
+
+  for (int t = 0; t < n_kv; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < n_kv) fetch(t + 1);
+
+    // ---- S^T = K Q^T for 64 keys: s[sub][r] is key 32*sub + 8*(r/4) + 4*hi + r%4
+    f32x16_t s[2];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[sub][r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8_t ka = __builtin_bit_cast(
+            bf16x8_t, *reinterpret_cast<const u32x4_t*>(&k_lds[buf][32 * sub + l32][ks * 16 + 8 * hi]));
+        s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[ks], s[sub], 0, 0, 0);
+      }
+    }
+
+    // ---- causal mask on diagonal tiles (keys past Lk are past every diagonal too)
+    if (t >= first_masked_tile) {
+      const int lim = diag - t * BN;  // key offsets <= lim are visible
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kofs = 32 * sub + 8 * (r >> 2) + 4 * hi + (r & 3);
+          if (kofs > lim) s[sub][r] = -INFINITY;
+        }
+    }
+
+    // ---- online softmax: row max over this lane's 32 keys and lane^32's
+    float mx = s[0][0];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sub][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m, mx);  // finite: key 0 of tile 0 is visible to every row
+    const float alpha = exp2f((m - m_new) * scale_log2);
+    const float mc = m_new * scale_log2;
+    m = m_new;
+    float psum = 0.f;
+    bf16x8_t pb[4];  // P^T operand of k-step ks = 2*sub + half
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        u32x4_t w;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const float p0 = exp2f(s[sub][8 * half + 2 * e2] * scale_log2 - mc);
+          const float p1 = exp2f(s[sub][8 * half + 2 * e2 + 1] * scale_log2 - mc);
+          psum += p0 + p1;
+          w[e2] = pack_bf16x2(p0, p1);
+        }
+        pb[2 * sub + half] = __builtin_bit_cast(bf16x8_t, w);
+      }
+    l = l * alpha + psum;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+
+    // ---- O^T += V^T P^T: A = V^T via transposing LDS reads, keys in the same order as P
+    const int g = lane >> 4;         // 16-lane group
+    const int gl = lane & 15;        // lane within the group
+    const int key_in = 4 * hi + (gl >> 2);
+    const int col_in = 16 * (g & 1) + 4 * (gl & 3);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const uint16_t* p0 = &v_lds[buf][16 * ks + key_in][32 * dt + col_in];
+        const i16x4_t lo4 = lds_read_tr16(p0);
+        const i16x4_t hi4 = lds_read_tr16(p0 + 8 * KP);
+        const u32x2_t lo = __builtin_bit_cast(u32x2_t, lo4);
+        const u32x2_t hi2 = __builtin_bit_cast(u32x2_t, hi4);
+        const u32x4_t va = {lo[0], lo[1], hi2[0], hi2[1]};
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, va), pb[ks],
+                                                       o[dt], 0, 0, 0);
+      }
+    }
+
+    if (t + 1 < n_kv) stage(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- normalise and store: o[dt][r] is d = 32*dt + 8*(r/4) + 4*hi + r%4 of this row
+  l += __shfl_xor(l, 32, 64);
+  if (row_valid) {
+    const float inv = 1.f / l;
+    uint16_t* orow = out + (static_cast<int64_t>(q_begin + tok) * Hq + hq) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        u32x2_t w;
+        w[0] = pack_bf16x2(o[dt][4 * r4] * inv, o[dt][4 * r4 + 1] * inv);
+        w[1] = pack_bf16x2(o[dt][4 * r4 + 2] * inv, o[dt][4 * r4 + 3] * inv);
+        *reinterpret_cast<u32x2_t*>(orow + 32 * dt + 8 * r4 + 4 * hi) = w;
+      }
+  }
+}
+
+template <int D, int GP>
+static void launch_prefill(dim3 grid, hipStream_t stream, const void* q, void* out,
+                           const void* kc, const void* vc, const int32_t* cu_q,
+                           const int32_t* cu_k, const int32_t* tables, int stride, int Hq,
+                           int Hkv, int G, int bs_log2, float scale_log2) {
+  hipLaunchKernelGGL((paged_prefill_bf16_kernel<D, GP>), grid, dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(q), static_cast<uint16_t*>(out),
+                     static_cast<const uint16_t*>(kc), static_cast<const uint16_t*>(vc), cu_q,
+                     cu_k, tables, stride, Hq, Hkv, G, bs_log2, scale_log2);
+}
+
+hipError_t launch_paged_prefill_bf16(int head_dim, const void* q, void* out, const void* k_cache,
+                                     const void* v_cache, int num_q_heads, int num_kv_heads,
+                                     int bs_log2, int batch, int max_seqlen_q,
+                                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                     const int32_t* block_tables, int table_stride, float scale,
+                                     hipStream_t stream) {
+  const int G = num_q_heads / num_kv_heads;
+  if (G > 128) return hipErrorInvalidConfiguration;
+  const int GP = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : G <= 8 ? 8 : G <= 16 ? 16 : G <= 32
+                 ? 32 : G <= 64 ? 64 : 128;
+  const int bm_tok = 128 / GP;
+  const int64_t xs = static_cast<int64_t>(batch) * num_kv_heads;
+  const int max_tiles = (max_seqlen_q + bm_tok - 1) / bm_tok;
+  if (xs > 0x7fffffff || max_tiles > 65535) return hipErrorInvalidConfiguration;
+  const dim3 grid(static_cast<unsigned>(xs), max_tiles);
+  const float scale_log2 = scale * kLog2e;
+#define PKV_PF(D_, GP_)                                                                       \
+  launch_prefill<D_, GP_>(grid, stream, q, out, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k, \
+                          block_tables, table_stride, num_q_heads, num_kv_heads, G, bs_log2,  \
+                          scale_log2)
+#define PKV_PF_GP(D_)                                  \
+  switch (GP) {                                        \
+    case 1: PKV_PF(D_, 1); break;                      \
+    case 2: PKV_PF(D_, 2); break;                      \
+    case 4: PKV_PF(D_, 4); break;                      \
+    case 8: PKV_PF(D_, 8); break;                      \
+    case 16: PKV_PF(D_, 16); break;                    \
+    case 32: PKV_PF(D_, 32); break;                    \
+    case 64: PKV_PF(D_, 64); break;                    \
+    default: PKV_PF(D_, 128); break;                   \
+  }
+  timing_begin("paged_prefill_mfma", stream);
+  if (head_dim == 128) {
+    PKV_PF_GP(128)
+  } else {
+    PKV_PF_GP(64)
+  }
+  timing_end(stream);
+#undef PKV_PF_GP
+#undef PKV_PF
+  return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -174,3 +174,29 @@ def test_decode_equals_last_prefill_row(pkv):
     wl.q[1] = wl.q[0][-1:].copy()
     got = _step(wl).outputs_numpy()
     assert_close(got["decode"][0], got["prefill"][L - 1], "bf16", "decode vs last prefill row")
+
+
+def test_output_rounding_is_nearest_even(pkv):
+    """Two keys with equal scores average two V rows; the exact means below sit on
+    bf16 rounding ties and just off them, so the stored output pins the single
+    final rounding to round-to-nearest-even (the oracle's value, rounded here)."""
+    S = workloads.SeqSpec
+    wl = workloads.custom("rne", "bf16", 2, 1, 128, 16,
+                          [S("decode", 2, 1), S("prefill", 2, 1)], seed=12)
+    rng = np.random.default_rng(12)
+    for i in range(2):
+        wl.k[i][:] = 0  # equal scores -> weights exactly 1/2
+        base = rng.integers(-200, 200, size=128).astype(np.float32) / 64.0  # bf16-exact
+        ulp = np.float32(2.0) ** (np.floor(np.log2(np.maximum(np.abs(base), 1 / 64))) - 7)
+        odd = rng.integers(0, 4, size=128).astype(np.float32)  # 0..3 ulps apart
+        v0, v1 = base, base + odd * ulp
+        wl.v[i][0, 0] = workloads.round_to_bf16_bits(v0)
+        wl.v[i][1, 0] = workloads.round_to_bf16_bits(v1)
+    got = _step(wl)
+    dec = got.out_decode.view(torch.int16).cpu().numpy().view(np.uint16)
+    pre = got.out_prefill.view(torch.int16).cpu().numpy().view(np.uint16)
+    ref = oracle.run_step(wl)
+    want_dec = workloads.round_to_bf16_bits(ref["decode"].astype(np.float32))
+    want_pre = workloads.round_to_bf16_bits(ref["prefill"].astype(np.float32))
+    assert np.array_equal(dec, want_dec), "decode output not rounded to nearest even"
+    assert np.array_equal(pre, want_pre), "prefill output not rounded to nearest even"
