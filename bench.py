@@ -33,7 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
-BF16_MFMA_PEAK_TFLOPS = 2516.6  # 256 CUs x 2.4 GHz x 4096 flop/clk/CU, dense
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (256 CUs x 2.4 GHz x 4096 flop/clk/CU)
 
 
 def parse():

@@ -4,9 +4,9 @@
  * The data plane of a nano-vLLM-style engine: the KV write through a slot
  * mapping, causal prefill over sequences packed by cumulative lengths that reads
  * cached blocks through block tables, and decode over block tables with context
- * lengths.  Pages: nano-vLLM, intelliparadigm article section 3.2
+ * lengths.  Pages: “Nano-vLLM 引擎架构解析” section 3.2
  * "PagedAttention" (fixed pool of 256-token blocks, ref-counted ids, block reuse
- * by prefix hash) and lnwmold article headings "From Sequences to Blocks",
+ * by prefix hash) and “深入 Nano-vLLM 推理引擎” headings "From Sequences to Blocks",
  * "Prefix Caching by hashing", "Control plane vs. data plane" (block metadata
  * lives on the CPU, KV data on the GPU, freed blocks are not cleared),
  * "Prefill and Decode" and "Preparing for computation" (prefill packs sequences
@@ -68,7 +68,7 @@ typedef struct {
   int32_t dtype; /* pkv_dtype */
 } pkv_cache;
 
-/* KV write (lnwmold, "Control plane vs. data plane": a reused block is simply
+/* KV write (“深入 Nano-vLLM 推理引擎”, "Control plane vs. data plane": a reused block is simply
  * overwritten).  For t in [0, num_tokens): if slot_mapping[t] >= 0, row
  * slot_mapping[t] of each cache receives k[t] / v[t] bit for bit; slot -1 (a
  * padding row) writes nothing.
@@ -81,7 +81,7 @@ pkv_status pkv_store_kvcache(const pkv_cache* cache, const void* k, const void* 
                              const int32_t* slot_mapping, int32_t num_tokens,
                              hipStream_t stream);
 
-/* Varlen causal prefill (lnwmold, "Preparing for computation": sequences are
+/* Varlen causal prefill (“深入 Nano-vLLM 推理引擎”, "Preparing for computation": sequences are
  * packed and addressed by cumulative lengths; "Prefix Caching": cached blocks
  * are read, not recomputed).  Sequence b owns query rows
  * cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 and Lk = cu_seqlens_k[b+1] -
@@ -113,7 +113,7 @@ size_t pkv_paged_decode_workspace_size(const pkv_cache* cache, int32_t num_q_hea
                                        int32_t batch, int32_t max_context_len,
                                        int32_t num_splits);
 
-/* Decode (lnwmold, "Prefill and Decode": one new token per sequence per step).
+/* Decode (“深入 Nano-vLLM 推理引擎”, "Prefill and Decode": one new token per sequence per step).
  * Sequence b's single query attends to its context_lens[b] cached tokens, the
  * new token's K/V (written beforehand) being the last.  Long contexts are cut
  * at block boundaries into splits that run in parallel and are merged exactly

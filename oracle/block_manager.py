@@ -1,7 +1,7 @@
 """Plain CPU model of the KV-cache control plane (test infrastructure only).
 
-Follows the BlockManager the pages describe (intelliparadigm article, section 3.2
-"PagedAttention"; lnwmold article, headings "Handling resource exhaustion",
+Follows the BlockManager the pages describe (“Nano-vLLM 引擎架构解析”, section 3.2
+"PagedAttention"; “深入 Nano-vLLM 推理引擎”, headings "Handling resource exhaustion",
 "From Sequences to Blocks", "Prefix Caching by hashing", "Control plane vs.
 data plane"):
 

@@ -1,7 +1,7 @@
 """Plain CPU definition of paged KV-cache attention (test infrastructure only).
 
-What is computed, and where the pages say so (nano-vLLM pages: the
-intelliparadigm article, section 3.2 "PagedAttention"; the lnwmold article,
+What is computed, and where the pages say so (“Nano-vLLM 引擎架构解析”,
+section 3.2 "PagedAttention"; “深入 Nano-vLLM 推理引擎”,
 headings "From Sequences to Blocks", "Prefix Caching by hashing",
 "Control plane vs. data plane", "Preparing for computation", "Prefill and
 Decode"):

@@ -2,8 +2,8 @@
 
 The step follows the pages' order for a batch: blocks are allocated by the
 control plane, the new tokens' K/V are written into their slots, then prefill
-runs over the prefill sequences and decode over the decode sequences (lnwmold
-article, headings "Prefill and Decode" and "Preparing for computation").  Tokens
+runs over the prefill sequences and decode over the decode sequences (“深入 Nano-vLLM 推理引擎”,
+headings "Prefill and Decode" and "Preparing for computation").  Tokens
 a sequence already had before the step (decode history, a cached prefix) are
 written by an earlier KV write.  Every slot that no token writes keeps the
 ``stale`` value, standing for whatever a freed block held before ("Control plane

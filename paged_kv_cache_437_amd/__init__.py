@@ -1,7 +1,6 @@
 """Paged KV-cache attention for AMD MI355X (gfx950): Python binding of libpkv.
 
-Three calls, the data plane of a nano-vLLM-style engine (nano-vLLM pages:
-intelliparadigm article section 3.2 "PagedAttention"; lnwmold article headings
+Three calls, the data plane of a nano-vLLM-style engine (“Nano-vLLM 引擎架构解析” section 3.2 "PagedAttention"; “深入 Nano-vLLM 推理引擎” headings
 "From Sequences to Blocks", "Control plane vs. data plane", "Prefill and
 Decode", "Preparing for computation"):
 

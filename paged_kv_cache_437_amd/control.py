@@ -1,8 +1,8 @@
 """Control plane: the KV block pool and the per-step device metadata.
 
-The pages put block bookkeeping on the CPU and KV data on the GPU (lnwmold
-article, "Control plane vs. data plane"): the pool hands out fixed-size blocks
-(256 tokens by default, intelliparadigm article section 3.2) from the head of a
+The pages put block bookkeeping on the CPU and KV data on the GPU (“深入 Nano-vLLM 推理引擎”,
+"Control plane vs. data plane"): the pool hands out fixed-size blocks
+(256 tokens by default, “Nano-vLLM 引擎架构解析” section 3.2) from the head of a
 free list, counts references so that sequences with a common prefix reuse the
 same block ids ("Prefix Caching by hashing"), and on release only marks a block
 free - its device contents stay until a later write overwrites them.  When no

@@ -1,6 +1,6 @@
 // Generic paged attention on the vector ALU: one wavefront per (query row, q head).
 //
-// What it computes is the plain definition (nano-vLLM pages, lnwmold article,
+// What it computes is the plain definition (“深入 Nano-vLLM 推理引擎”,
 // "Prefill and Decode" and "Preparing for computation"): for sequence b, query i of
 // its Lq new tokens sits at position Lk - Lq + i and attends, with a softmax of
 // scale * q.k, to keys 0 .. Lk - Lq + i read through the block table.  Decode is the

@@ -1,6 +1,6 @@
 // Paged decode attention, bf16 in / fp32 accumulate, for gfx950.
 //
-// What is computed (nano-vLLM pages, lnwmold article, "Prefill and Decode": each
+// What is computed (“深入 Nano-vLLM 推理引擎”, "Prefill and Decode": each
 // decode step adds one token per sequence; "From Sequences to Blocks": a sequence's
 // tokens live in the blocks its table lists): for sequence b and q head h,
 //   out[b, h] = softmax_j(scale * q[b, h] . k_j) v_j   over j < context_lens[b],

@@ -1,6 +1,6 @@
 // Paged varlen causal prefill, bf16 in / fp32 accumulate, on gfx950 MFMA.
 //
-// What is computed (nano-vLLM pages, lnwmold article, "Preparing for computation":
+// What is computed (“深入 Nano-vLLM 推理引擎”, "Preparing for computation":
 // prefill packs sequences and addresses them by cumulative lengths; "Prefix Caching
 // by hashing": a cached prefix is read from its shared blocks, not recomputed):
 // sequence b owns query rows cu_q[b] .. cu_q[b+1]-1 (Lq of them) and Lk keys read

@@ -1,4 +1,4 @@
-// KV write through a slot mapping (nano-vLLM pages, lnwmold article, "Control plane
+// KV write through a slot mapping (“深入 Nano-vLLM 推理引擎”, "Control plane
 // vs. data plane": the data plane only copies rows into the slots the control plane
 // chose; a reused block is overwritten, never cleared first).
 //

@@ -7,8 +7,8 @@ holds none of the method's arithmetic: no slot arithmetic, no block tables, no
 attention.  Turning a workload into block tables and slot mappings is the
 control plane's job; computing attention is the kernels' (and the oracle's).
 
-Sources for the shapes (nano-vLLM pages, "PagedAttention" section of the
-intelliparadigm article and the "Block Manager" headings of the lnwmold article):
+Sources for the shapes ("PagedAttention" section of
+“Nano-vLLM 引擎架构解析” and the "Block Manager" headings of the “深入 Nano-vLLM 推理引擎”):
 KV memory is a fixed pool of blocks of 256 tokens by default; a long sequence
 spans several blocks; sequences sharing a prefix share ref-counted block ids;
 prefill packs a batch of sequences by cumulative lengths and decode adds one
