@@ -106,35 +106,41 @@ pkv_status pkv_paged_prefill(const pkv_cache* cache, const void* q, void* out,
                              const int32_t* block_tables, int32_t block_table_stride,
                              float scale, hipStream_t stream);
 
-/* Bytes of device workspace pkv_paged_decode needs for this shape (0 when a
- * single split covers max_context_len).  num_splits as in pkv_paged_decode.
- * Returns 0 for invalid arguments. */
+/* Bytes of device workspace pkv_paged_decode needs for this shape; num_workers as
+ * in pkv_paged_decode.  0 for the fp32 path (it needs none) and for invalid
+ * arguments.  For bf16: 2*W*GP*(4*head_dim + 8) + 8*(batch + 1) bytes, rounded up
+ * to 256-byte pieces, with W = num_workers (4096 when 0) and GP = q heads per kv
+ * head rounded up to a power of two, at most 8 (about 4.3 MB at GP 1, head_dim 128
+ * and W = 4096).  max_context_len does not change it. */
 size_t pkv_paged_decode_workspace_size(const pkv_cache* cache, int32_t num_q_heads,
                                        int32_t batch, int32_t max_context_len,
-                                       int32_t num_splits);
+                                       int32_t num_workers);
 
 /* Decode (“深入 Nano-vLLM 推理引擎”, "Prefill and Decode": one new token per sequence per step).
  * Sequence b's single query attends to its context_lens[b] cached tokens, the
- * new token's K/V (written beforehand) being the last.  Long contexts are cut
- * at block boundaries into splits that run in parallel and are merged exactly
- * (log-sum-exp) in a second kernel.
+ * new token's K/V (written beforehand) being the last.
  *   q, out          [batch][num_q_heads][head_dim]
  *   context_lens    [batch] int32, each in [1, max_context_len]
- *   max_context_len host upper bound on context_lens (sizes grid and workspace)
+ *   max_context_len host upper bound on context_lens
  *   block_tables    [batch][block_table_stride] int32
  *   workspace       device scratch of at least
  *                   pkv_paged_decode_workspace_size(...) bytes (may be NULL when
  *                   that size is 0); contents on entry are ignored
- *   num_splits      0: split length chosen from max_context_len alone;
- *                   S > 0: at most S splits per sequence
- * The split boundaries depend only on lengths, never on block ids, so results
- * are bit-identical under any relabelling of physical blocks. */
+ *   num_workers     bf16: the K/V stream of every (sequence, kv head) is cut into
+ *                   16-token chunks and the list of all chunks is divided evenly
+ *                   among this many wavefront workers; a (sequence, kv head) cut
+ *                   between workers is merged exactly (log-sum-exp) by a second
+ *                   kernel.  0 = as many workers as the device holds resident
+ *                   (at most 4096); W in [1, 2^20] = exactly W (1 = no cut at all).
+ *                   Ignored by the fp32 path, which never cuts.
+ * The cut depends only on lengths and the worker count, never on block ids, so
+ * results are bit-identical under any relabelling of physical blocks. */
 pkv_status pkv_paged_decode(const pkv_cache* cache, const void* q, void* out,
                             int32_t num_q_heads, int32_t batch,
                             const int32_t* context_lens, int32_t max_context_len,
                             const int32_t* block_tables, int32_t block_table_stride,
                             float scale, void* workspace, size_t workspace_bytes,
-                            int32_t num_splits, hipStream_t stream);
+                            int32_t num_workers, hipStream_t stream);
 
 /* Kernel timing, off by default (tracing support for benchmarks).  While on,
  * every kernel the library launches is bracketed by two hipEvents recorded on

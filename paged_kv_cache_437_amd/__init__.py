@@ -7,8 +7,8 @@ Decode", "Preparing for computation"):
 * ``store_kvcache``  - write new tokens' K/V into their slots;
 * ``paged_prefill``  - varlen causal attention over packed sequences, K/V read
   from the cache through block tables (cached prefix blocks included);
-* ``paged_decode``   - one query per sequence over its cached context, split
-  over blocks and merged.
+* ``paged_decode``   - one query per sequence over its cached context, streamed
+  by wavefront workers over 16-token chunks and merged where a context is cut.
 
 This module only marshals arguments: shapes, dtypes and devices are checked,
 pointers and torch's current stream are handed to the C ABI, and every step of
@@ -127,15 +127,15 @@ def paged_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
 
 
 def paged_decode_workspace_size(k_cache: torch.Tensor, v_cache: torch.Tensor, num_q_heads: int,
-                                batch: int, max_context_len: int, num_splits: int = 0) -> int:
+                                batch: int, max_context_len: int, num_workers: int = 0) -> int:
     desc = _cache_desc(k_cache, v_cache)
     return int(_lib.load().pkv_paged_decode_workspace_size(
-        ctypes.byref(desc), num_q_heads, batch, max_context_len, num_splits))
+        ctypes.byref(desc), num_q_heads, batch, max_context_len, num_workers))
 
 
 def paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                  block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
-                 scale: float, num_splits: int = 0, out: torch.Tensor | None = None,
+                 scale: float, num_workers: int = 0, out: torch.Tensor | None = None,
                  workspace: torch.Tensor | None = None) -> torch.Tensor:
     """q [B, Hq, D] -> out [B, Hq, D]; one query per sequence over its context."""
     lib = _lib.load()
@@ -150,7 +150,7 @@ def paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     elif out.shape != q.shape:
         raise ValueError("out must have q's shape")
     need = lib.pkv_paged_decode_workspace_size(ctypes.byref(desc), q.shape[1], batch,
-                                               int(max_context_len), int(num_splits))
+                                               int(max_context_len), int(num_workers))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
@@ -158,6 +158,6 @@ def paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     args = (_dev(q, "q", k_cache.dtype, k_cache), _dev(out, "out", k_cache.dtype, k_cache),
             q.shape[1], batch, _dev(context_lens, "context_lens", torch.int32, k_cache),
             int(max_context_len), _dev(block_tables, "block_tables", torch.int32, k_cache),
-            block_tables.shape[1], float(scale), ws_ptr, ws_bytes, int(num_splits))
+            block_tables.shape[1], float(scale), ws_ptr, ws_bytes, int(num_workers))
     _lib.check(lib.pkv_paged_decode(ctypes.byref(desc), *args, _stream(k_cache.device)))
     return out

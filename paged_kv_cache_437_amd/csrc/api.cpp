@@ -63,6 +63,9 @@ pkv_status launched(hipError_t e, const char* what) {
 
 size_t elem_size(const pkv_cache* c) { return c->dtype == PKV_F32 ? 4 : 2; }
 
+// upper bound on an explicit decode worker count (the automatic count is at most 4096)
+constexpr int32_t kMaxWorkers = 1 << 20;
+
 }  // namespace
 
 extern "C" {
@@ -80,7 +83,7 @@ const char* pkv_status_string(pkv_status s) {
 
 const char* pkv_last_error(void) { return g_last_error; }
 
-int32_t pkv_version(void) { return 100; }
+int32_t pkv_version(void) { return 200; }
 
 pkv_status pkv_store_kvcache(const pkv_cache* cache, const void* k, const void* v,
                              const int32_t* slot_mapping, int32_t num_tokens,
@@ -140,16 +143,15 @@ pkv_status pkv_paged_prefill(const pkv_cache* cache, const void* q, void* out,
 
 size_t pkv_paged_decode_workspace_size(const pkv_cache* cache, int32_t num_q_heads,
                                        int32_t batch, int32_t max_context_len,
-                                       int32_t num_splits) {
+                                       int32_t num_workers) {
   if (cache == nullptr || num_q_heads <= 0 || batch <= 0 || max_context_len <= 0 ||
-      num_splits < 0)
+      num_workers < 0 || num_workers > kMaxWorkers || cache->num_kv_heads <= 0 ||
+      num_q_heads % cache->num_kv_heads != 0 ||
+      (cache->head_dim != 64 && cache->head_dim != 128))
     return 0;
-  if (cache->dtype != PKV_BF16) return 0;  // the fp32 path runs unsplit
-  int split_tokens = 0, max_splits = 0;
-  pkv::decode_split_plan(max_context_len, num_splits, &split_tokens, &max_splits);
-  if (max_splits <= 1) return 0;
-  const size_t n = static_cast<size_t>(batch) * num_q_heads * max_splits;
-  return n * static_cast<size_t>(cache->head_dim) * sizeof(float) + n * 2 * sizeof(float);
+  if (cache->dtype != PKV_BF16) return 0;  // the fp32 path needs none
+  return pkv::paged_decode_bf16_workspace(cache->head_dim, num_q_heads, cache->num_kv_heads,
+                                          batch, num_workers);
 }
 
 pkv_status pkv_paged_decode(const pkv_cache* cache, const void* q, void* out,
@@ -157,12 +159,14 @@ pkv_status pkv_paged_decode(const pkv_cache* cache, const void* q, void* out,
                             const int32_t* context_lens, int32_t max_context_len,
                             const int32_t* block_tables, int32_t block_table_stride,
                             float scale, void* workspace, size_t workspace_bytes,
-                            int32_t num_splits, hipStream_t stream) {
+                            int32_t num_workers, hipStream_t stream) {
   pkv_status st = check_cache(cache);
   if (st != PKV_OK) return st;
   if ((st = check_heads(cache, num_q_heads)) != PKV_OK) return st;
-  if (batch < 0 || max_context_len < 0 || block_table_stride < 0 || num_splits < 0)
-    return fail(PKV_ERR_INVALID, "negative batch / max_context_len / stride / num_splits");
+  if (batch < 0 || max_context_len < 0 || block_table_stride < 0 || num_workers < 0)
+    return fail(PKV_ERR_INVALID, "negative batch / max_context_len / stride / num_workers");
+  if (num_workers > kMaxWorkers)
+    return fail(PKV_ERR_INVALID, "num_workers %d > %d", num_workers, kMaxWorkers);
   if (batch > 65535) return fail(PKV_ERR_UNSUPPORTED, "batch %d > 65535", batch);
   if (batch == 0) return ok();
   if (max_context_len == 0) return fail(PKV_ERR_INVALID, "max_context_len is 0");
@@ -176,19 +180,16 @@ pkv_status pkv_paged_decode(const pkv_cache* cache, const void* q, void* out,
   if (!(scale > 0.f) || !std::isfinite(scale))
     return fail(PKV_ERR_INVALID, "scale %g must be finite and positive", scale);
   const size_t ws = pkv_paged_decode_workspace_size(cache, num_q_heads, batch, max_context_len,
-                                                    num_splits);
+                                                    num_workers);
   if (ws > 0 && (workspace == nullptr || workspace_bytes < ws))
     return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, ws);
   const int bs_log2 = log2_exact(cache->block_size);
-  if (cache->dtype == PKV_BF16) {
-    int split_tokens = 0, max_splits = 0;
-    pkv::decode_split_plan(max_context_len, num_splits, &split_tokens, &max_splits);
+  if (cache->dtype == PKV_BF16)
     return launched(pkv::launch_paged_decode_bf16(
                         cache->head_dim, q, out, cache->k_cache, cache->v_cache, num_q_heads,
                         cache->num_kv_heads, bs_log2, batch, context_lens, block_tables,
-                        block_table_stride, scale, split_tokens, max_splits, workspace, stream),
+                        block_table_stride, scale, num_workers, workspace, stream),
                     "paged_decode");
-  }
   return launched(pkv::launch_attention_generic(
                       false, cache->head_dim, q, out, cache->k_cache, cache->v_cache,
                       num_q_heads, cache->num_kv_heads, bs_log2, batch, 1, nullptr, nullptr,

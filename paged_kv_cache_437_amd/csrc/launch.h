@@ -23,19 +23,19 @@ hipError_t launch_attention_generic(bool bf16, int head_dim, const void* q, void
                                     const int32_t* context_lens, const int32_t* block_tables,
                                     int table_stride, float scale, hipStream_t stream);
 
-// Split plan of the bf16 decode: splits of `split_tokens` tokens (a multiple of 256),
-// at most `max_splits` per sequence.  num_splits == 0 picks 256-token splits.
-void decode_split_plan(int max_context_len, int num_splits, int* split_tokens, int* max_splits);
-
-// bf16 paged decode: split kernel (+ combine kernel when max_splits > 1).  The
-// workspace holds [batch][Hq][max_splits][head_dim] float partial outputs followed by
-// [batch][Hq][max_splits] float2 (max, sum) pairs; unused when max_splits == 1.
+// bf16 paged decode: the streaming kernel over `num_workers` wavefront workers (0 =
+// as many as the device holds resident) and the combine kernel for streams cut
+// between workers.  The workspace holds, 256-byte aligned one after the other:
+// int64 [batch+1] first chunk of each sequence, float2 [2W][GP] (max, sum) and
+// float [2W][GP][head_dim] partial outputs, W the worker count and GP the q heads
+// per stream; paged_decode_bf16_workspace gives its size.
+size_t paged_decode_bf16_workspace(int head_dim, int num_q_heads, int num_kv_heads, int batch,
+                                   int num_workers);
 hipError_t launch_paged_decode_bf16(int head_dim, const void* q, void* out, const void* k_cache,
                                     const void* v_cache, int num_q_heads, int num_kv_heads,
                                     int bs_log2, int batch, const int32_t* context_lens,
                                     const int32_t* block_tables, int table_stride, float scale,
-                                    int split_tokens, int max_splits, void* workspace,
-                                    hipStream_t stream);
+                                    int num_workers, void* workspace, hipStream_t stream);
 
 // bf16 varlen causal prefill on MFMA (one launch).
 hipError_t launch_paged_prefill_bf16(int head_dim, const void* q, void* out, const void* k_cache,

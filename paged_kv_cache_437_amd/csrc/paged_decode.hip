@@ -6,27 +6,41 @@
 //   out[b, h] = softmax_j(scale * q[b, h] . k_j) v_j   over j < context_lens[b],
 // with k_j, v_j the rows of kv head h / (Hq / Hkv) found through block_tables[b].
 //
-// Work decomposition.  The context is cut into splits of `split_tokens` tokens (a
-// multiple of 256 and hence of every supported block size), so the cut depends only
-// on lengths.  One workgroup of 4 wavefronts handles (split, kv head, group of up to
-// 8 q heads, sequence); it walks its split 256 tokens at a time, wave w taking tokens
-// 64w .. 64w+63 of each 256.  Per wave and 64 tokens:
+// The pass is a stream over HBM: every K/V byte is read once, so the design is about
+// keeping loads in flight without gaps, not about arithmetic.
+//
+// Work decomposition.  A "stream" is (sequence, kv head, group of up to GP q heads
+// of that kv head); it is cut into chunks of CH tokens.  All chunks of all streams,
+// in (sequence, stream, position) order, form one list of C chunks that is divided
+// evenly among W independent wavefront workers (worker w takes chunks
+// [w*C/W, (w+1)*C/W)), W being as many waves as the device holds resident.  Each
+// worker walks its range with two register buffers: the K/V loads of chunk c+1 (and
+// the block-table entry of chunk c+2) are issued before chunk c is computed, so HBM
+// sees a continuous stream.  K/V are read with non-temporal loads: they are used
+// once, and streaming them past the caches is what lets the read approach the HBM
+// peak.  The cut depends only on lengths and W, never on block ids.
+//
+// Per chunk and worker:
 //   * K rows go straight from HBM into the B operand of v_mfma_f32_16x16x32_bf16
 //     (lane: token lane%16, 8 head_dim elements), the A operand holding the group's
-//     q rows (padded to 16), so the 16x16 score tiles cost four MFMAs per 16 tokens;
-//     every q head of the group reuses each K row loaded.
-//   * Online softmax in the log2 domain (scale * log2 e folded into one multiply):
-//     row max across the 16 lanes of a tile row, exp2, per-lane partial sums.
-//   * Probabilities go through a per-wave LDS tile to the P.V phase, where lanes own
-//     (token, 8 head_dim elements) of V rows loaded with 16-byte loads and accumulate
-//     on the vector ALU.
+//     q rows (padded to 16), so every grouped q head reuses each K row loaded;
+//   * online softmax in the log2 domain (scale * log2 e folded into one multiply):
+//     row max across the 16 lanes of a tile row, exp2, per-lane partial sums;
+//   * probabilities go through a per-wave LDS tile to the P.V phase, where lanes
+//     own (token, 8 head_dim elements) of V rows loaded with 16-byte loads and
+//     accumulate on the vector ALU.
 // All K/V loads are predicated on token < context_len, so neither table entries past
 // the last used block nor the stale tail of the last block is ever read.
-// The four waves' (max, sum, unnormalised out) merge exactly in LDS; a sequence with
-// one split writes its output directly, otherwise the partial goes to the workspace
-// and decode_combine merges the splits:  M = max_s m_s,
-//   out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,  rounded once to bf16.
+//
+// A stream whose chunks all fall to one worker is finished by it and written as
+// bf16.  A stream cut between workers leaves one fp32 partial (max, sum,
+// unnormalised out) per worker in the workspace, and decode_combine merges them
+// exactly, in worker order:  M = max_w m_w,
+//   out = sum_w 2^(m_w - M) o_w / sum_w 2^(m_w - M) l_w,  rounded once to bf16.
 // No atomics: results are bit-identical across runs and block relabellings.
+#include <algorithm>
+#include <atomic>
+
 #include "device.h"
 #include "launch.h"
 #include "timing.h"
@@ -35,171 +49,304 @@ namespace pkv {
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
+namespace {
+
+// Reductions over the 16 lanes of a row with DPP lane moves (quad swaps, then the
+// half-row and row mirrors): every lane of the row ends with the result.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float row16_max(float x) {
-  x = fmaxf(x, __shfl_xor(x, 1, 64));
-  x = fmaxf(x, __shfl_xor(x, 2, 64));
-  x = fmaxf(x, __shfl_xor(x, 4, 64));
-  x = fmaxf(x, __shfl_xor(x, 8, 64));
-  return x;
+  x = fmaxf(x, dpp<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp<0x141>(x));  // row_half_mirror
+  return fmaxf(x, dpp<0x140>(x));  // row_mirror
 }
 __device__ __forceinline__ float row16_sum(float x) {
-  x += __shfl_xor(x, 1, 64);
-  x += __shfl_xor(x, 2, 64);
-  x += __shfl_xor(x, 4, 64);
-  x += __shfl_xor(x, 8, 64);
-  return x;
+  x += dpp<0xB1>(x);
+  x += dpp<0x4E>(x);
+  x += dpp<0x141>(x);
+  return x + dpp<0x140>(x);
 }
 __device__ __forceinline__ float read_lane(float x, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
 }
+__device__ __forceinline__ int64_t read_lane64(int64_t x, int lane) {
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(x), lane);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(x >> 32), lane);
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+__device__ __forceinline__ int64_t shfl_up64(int64_t x, int d) {
+  const int lo = __shfl_up(static_cast<int>(x), d, 64);
+  const int hi = __shfl_up(static_cast<int>(x >> 32), d, 64);
+  return static_cast<int64_t>((static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) |
+                              static_cast<uint32_t>(lo));
+}
+__device__ __forceinline__ int64_t wave_sum64(int64_t x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const int lo = __shfl_xor(static_cast<int>(x), o, 64);
+    const int hi = __shfl_xor(static_cast<int>(x >> 32), o, 64);
+    x += static_cast<int64_t>((static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) |
+                              static_cast<uint32_t>(lo));
+  }
+  return x;
+}
 
-template <int D, int GP>
-__global__ __launch_bounds__(256, 2) void paged_decode_bf16_kernel(
+// K/V rows are read once: non-temporal loads stream them past the caches.
+__device__ __forceinline__ u32x4_t load_stream(const uint16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+// Wavefront-uniform base plus a 32-bit per-lane byte offset: one address register
+// per lane and the scalar-base form of the load.
+__device__ __forceinline__ u32x4_t load_stream(const uint16_t* base, uint32_t byte_off) {
+  return __builtin_nontemporal_load(
+      reinterpret_cast<const u32x4_t*>(reinterpret_cast<const char*>(base) + byte_off));
+}
+
+// chunks of a sequence of length L
+template <int CH>
+__device__ __forceinline__ int chunks_of(int L) {
+  return (max(L, 0) + CH - 1) / CH;
+}
+
+// worker owning chunk c of C when C chunks are split over W workers as [w*C/W, (w+1)*C/W)
+__device__ __forceinline__ int64_t worker_of(int64_t c, int64_t C, int64_t W) {
+  return ((c + 1) * W - 1) / C;
+}
+
+// Position of a worker in the chunk list; every field is wavefront-uniform.
+struct Cursor {
+  int b;    // sequence
+  int L;    // its context length
+  int nch;  // its chunks per stream
+  int j;    // stream within the sequence: kv head * n_hg + head group
+  int k;    // chunk within the stream
+};
+
+// One chunk's operands in registers: K rows as MFMA B operands, V rows as 16-byte
+// (token, 8 head_dim elements) pieces, and the stream's q rows as the A operand.
+template <int D, int CH>
+struct KVBuf {
+  u32x4_t k[CH / 16][D / 32];
+  u32x4_t v[CH * (D / 8) / 64];
+  u32x4_t q[D / 32];
+};
+
+}  // namespace
+
+template <int D, int GP, int CH, bool ONE_BLOCK>
+__global__ __launch_bounds__(256) void paged_decode_bf16_kernel(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
     const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ block_tables,
-    int table_stride, int Hq, int Hkv, int G, int n_hg, int bs_log2, int split_tokens,
-    int max_splits, float scale_log2, float* __restrict__ ws_o, float2* __restrict__ ws_ml) {
+    int table_stride, int batch, int Hq, int Hkv, int G, int n_hg, int bs_log2,
+    float scale_log2, int num_workers, int64_t* __restrict__ ws_prefix,
+    float2* __restrict__ ws_ml, float* __restrict__ ws_o) {
   static_assert(D == 64 || D == 128, "head_dim");
-  static_assert(GP == 1 || GP == 2 || GP == 4 || GP == 8, "heads per workgroup");
-  constexpr int KK = D / 32;     // MFMA k-steps over head_dim
-  constexpr int DCH = D / 8;     // 16-byte chunks per row
-  constexpr int TPI = 64 / DCH;  // tokens per V load instruction of a wave
-  constexpr int VIT = 64 / TPI;  // V load instructions per wave per 64 tokens
+  static_assert(GP == 1 || GP == 2 || GP == 4 || GP == 8, "heads per stream");
+  static_assert(CH == 16 || CH == 32, "chunk");
+  constexpr int KK = D / 32;           // MFMA k-steps over head_dim
+  constexpr int DCH = D / 8;           // 16-byte pieces per row
+  constexpr int TPI = 64 / DCH;        // tokens per V load instruction
+  constexpr int VIT = CH / TPI;        // V loads per lane per chunk
+  constexpr int T16 = CH / 16;         // 16-token score tiles per chunk
+  constexpr int RR = GP < 4 ? GP : 4;  // head rows a lane keeps softmax state for
+  typedef KVBuf<D, CH> Buf;
 
-  __shared__ __attribute__((aligned(16))) float p_lds[4][64][16];
-  __shared__ __attribute__((aligned(16))) float o_lds[4][GP][D];
-  __shared__ float m_lds[4][16];
-  __shared__ float l_lds[4][16];
+  __shared__ __attribute__((aligned(16))) float p_lds[4][CH][16];
 
-  const int split = blockIdx.x;
-  const int kvh = blockIdx.y / n_hg;
-  const int hg = blockIdx.y - kvh * n_hg;
-  const int b = blockIdx.z;
-  const int L = context_lens[b];
-  const int n_splits = (L + split_tokens - 1) / split_tokens;
-  if (split >= n_splits) return;  // uniform over the workgroup, before any barrier
-
-  const int wave = threadIdx.x >> 6;
+  // wave index through readfirstlane: the compiler then knows everything derived
+  // from it (the worker's chunk range and cursor) is wavefront-uniform
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
+  const int worker = blockIdx.x * 4 + wave;
+  if (worker >= num_workers) return;  // wavefront-uniform; the kernel has no block barrier
   const int row = lane & 15;  // MFMA: token column (B) / head row (A)
-  const int grp = lane >> 4;  // MFMA: which 8-element slice of each 32-wide k-step
-  const int h0 = kvh * G + hg * GP;
-  const int nh = min(GP, G - hg * GP);
-  const int32_t* table = block_tables + static_cast<int64_t>(b) * table_stride;
-  const int bs_mask = (1 << bs_log2) - 1;
-
-  // q rows of the group as the MFMA A operand; rows >= nh are zero
-  bf16x8_t qa[KK];
-#pragma unroll
-  for (int kk = 0; kk < KK; ++kk) {
-    u32x4_t w = {0u, 0u, 0u, 0u};
-    if (row < nh)
-      w = *reinterpret_cast<const u32x4_t*>(q + (static_cast<int64_t>(b) * Hq + h0 + row) * D +
-                                            kk * 32 + grp * 8);
-    qa[kk] = __builtin_bit_cast(bf16x8_t, w);
-  }
-
-  float m_r[4], l_r[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    m_r[r] = -INFINITY;
-    l_r[r] = 0.f;
-  }
-  float o[GP][8];
-#pragma unroll
-  for (int h = 0; h < GP; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
-
+  const int grp = lane >> 4;  // MFMA: 8-element slice of each 32-wide k-step
   const int v_chunk = lane % DCH;
   const int v_sub = lane / DCH;
-  const int split_end = min(L, (split + 1) * split_tokens);
+  const int S = Hkv * n_hg;
+  const int bs_mask = (1 << bs_log2) - 1;
+  const uint32_t row_bytes = static_cast<uint32_t>(Hkv) * D * 2;  // token stride in a block
 
-  for (int c0 = split * split_tokens; c0 < split_end; c0 += 256) {
-    const int base = c0 + 64 * wave;  // first token of this wave's 64
-    if (base >= L) continue;          // nothing valid for this wave (no barrier inside)
-
-    // ---- issue every K and V load of the 64 tokens
-    u32x4_t kb[4][KK];
-    u32x4_t vb[VIT];
-    if (bs_log2 >= 6) {
-      // a 64-aligned run of 64 tokens lies in one block: one table entry per wave
-      const int64_t blk = table[base >> bs_log2];
-      const int64_t first = ((blk << bs_log2) | (base & bs_mask)) * Hkv + kvh;
+  // ---- the chunk list: its length, then this worker's first sequence.  Worker 0
+  // also records every sequence's first chunk for the combine kernel.
+  int64_t tot = 0;
+  for (int b0 = 0; b0 < batch; b0 += 64)
+    if (b0 + lane < batch) tot += static_cast<int64_t>(chunks_of<CH>(context_lens[b0 + lane])) * S;
+  const int64_t C = read_lane64(wave_sum64(tot), 0);
+  const int64_t W = num_workers;
+  const int64_t c_begin = worker * C / W;
+  const int64_t c_end = (worker + 1) * C / W;
+  int b_first = -1;
+  int64_t p_first = 0;
+  {
+    int64_t carry = 0;
+    for (int b0 = 0; b0 < batch; b0 += 64) {
+      const int b = b0 + lane;
+      const int64_t n = b < batch ? static_cast<int64_t>(chunks_of<CH>(context_lens[b])) * S : 0;
+      int64_t incl = n;
 #pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4) {
-        const int tok = base + 16 * t4 + row;
-        const int64_t off = (first + static_cast<int64_t>(16 * t4 + row) * Hkv) * D + grp * 8;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          u32x4_t w = {0u, 0u, 0u, 0u};
-          if (tok < L) w = *reinterpret_cast<const u32x4_t*>(k_cache + off + kk * 32);
-          kb[t4][kk] = w;
+      for (int o = 1; o < 64; o <<= 1) {
+        const int64_t t = shfl_up64(incl, o);
+        if (lane >= o) incl += t;
+      }
+      const int64_t excl = carry + incl - n;
+      if (worker == 0 && b < batch) ws_prefix[b] = excl;
+      if (b_first < 0) {
+        const uint64_t hit = __ballot(n > 0 && excl <= c_begin && c_begin < excl + n);
+        if (hit) {
+          const int ln = __builtin_ctzll(hit);
+          b_first = b0 + ln;
+          p_first = read_lane64(excl, ln);
         }
       }
-#pragma unroll
-      for (int it = 0; it < VIT; ++it) {
-        const int tl = it * TPI + v_sub;
-        u32x4_t w = {0u, 0u, 0u, 0u};
-        if (base + tl < L)
-          w = *reinterpret_cast<const u32x4_t*>(
-              v_cache + (first + static_cast<int64_t>(tl) * Hkv) * D + v_chunk * 8);
-        vb[it] = w;
-      }
-    } else {
-#pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4) {
-        const int tok = base + 16 * t4 + row;
-        int64_t off = 0;
-        if (tok < L) off = token_row(table[tok >> bs_log2], tok, bs_log2, Hkv, kvh, D) + grp * 8;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          u32x4_t w = {0u, 0u, 0u, 0u};
-          if (tok < L) w = *reinterpret_cast<const u32x4_t*>(k_cache + off + kk * 32);
-          kb[t4][kk] = w;
-        }
-      }
-#pragma unroll
-      for (int it = 0; it < VIT; ++it) {
-        const int tok = base + it * TPI + v_sub;
-        u32x4_t w = {0u, 0u, 0u, 0u};
-        if (tok < L)
-          w = *reinterpret_cast<const u32x4_t*>(
-              v_cache + token_row(table[tok >> bs_log2], tok, bs_log2, Hkv, kvh, D) +
-              v_chunk * 8);
-        vb[it] = w;
+      carry += read_lane64(incl, 63);
+      if (worker != 0 && b_first >= 0) break;
+    }
+    if (worker == 0 && lane == 0) ws_prefix[batch] = C;
+  }
+  if (c_begin >= c_end) return;
+
+  Cursor cur;
+  cur.b = b_first;
+  cur.L = context_lens[b_first];
+  cur.nch = chunks_of<CH>(cur.L);
+  {
+    const int64_t r = c_begin - p_first;
+    cur.j = static_cast<int>(r / cur.nch);
+    cur.k = static_cast<int>(r - static_cast<int64_t>(cur.j) * cur.nch);
+  }
+  auto advance = [&](Cursor& x) {
+    if (++x.k == x.nch) {
+      x.k = 0;
+      if (++x.j == S) {
+        x.j = 0;
+        do {  // the list holds a later chunk, so a sequence with chunks follows
+          ++x.b;
+          x.L = context_lens[x.b];
+          x.nch = chunks_of<CH>(x.L);
+        } while (x.nch == 0);
       }
     }
-
-    // ---- scores: S[head 4*grp + r][token 16*t4 + row] in acc[t4][r]
-    f32x4_t acc[4];
+  };
+  // Block id of this lane's token of the chunk (a vector load, so its wait counts in
+  // order with the K/V loads); with ONE_BLOCK every lane gets the same id.
+  auto table_entry = [&](const Cursor& x) -> int {
+    const int tok = min(x.k * CH + (lane & (CH - 1)), x.L - 1);
+    return block_tables[static_cast<int64_t>(x.b) * table_stride + (tok >> bs_log2)];
+  };
+  // Every load of a chunk is issued without a condition, so the compiler's waits
+  // count them in order: rows past the context re-read the chunk's last valid row
+  // (real data, never stale memory; their scores are masked and their V rows get
+  // weight 0), q rows past the stream's heads re-read its first row (zeroed when
+  // used), and a `live` == false chunk (the one after a worker's last) reads one row.
+  auto issue = [&](const Cursor& x, int te, Buf& buf, bool live) {
+    const int kvh = n_hg == 1 ? x.j : x.j / n_hg;
+    const int hg = x.j - kvh * n_hg;
+    const int tok0 = x.k * CH;
+    const int last = live ? min(x.L - tok0, CH) - 1 : 0;  // last row read
+    {
+      const uint16_t* qb = q + (static_cast<int64_t>(x.b) * Hq + kvh * G + hg * GP) * D;
+      const int qrow = (live && row < min(GP, G - hg * GP)) ? row : 0;
+      const uint32_t off = static_cast<uint32_t>(qrow * D + grp * 8) * 2;
 #pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) {
+      for (int kk = 0; kk < KK; ++kk)
+        buf.q[kk] = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const char*>(qb) + off +
+                                                      kk * 64);
+    }
+    if constexpr (ONE_BLOCK) {
+      // block_size >= CH: the chunk lies in one block, so a uniform base and 32-bit
+      // lane offsets address it
+      const int64_t blk = __builtin_amdgcn_readfirstlane(te);
+      const int64_t first = ((blk << bs_log2) | (tok0 & bs_mask)) * Hkv + kvh;
+      const uint16_t* kb = k_cache + first * D;
+      const uint16_t* vb = v_cache + first * D;
+#pragma unroll
+      for (int t4 = 0; t4 < T16; ++t4) {
+        const uint32_t off = static_cast<uint32_t>(min(16 * t4 + row, last)) * row_bytes + grp * 16;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) buf.k[t4][kk] = load_stream(kb, off + kk * 64);
+      }
+#pragma unroll
+      for (int it = 0; it < VIT; ++it)
+        buf.v[it] = load_stream(
+            vb, static_cast<uint32_t>(min(it * TPI + v_sub, last)) * row_bytes + v_chunk * 16);
+    } else {
+      // small blocks: lane t holds the block of token tok0 + t
+#pragma unroll
+      for (int t4 = 0; t4 < T16; ++t4) {
+        const int tl = min(16 * t4 + row, last);
+        const int64_t off =
+            token_row(__shfl(te, tl, 64), tok0 + tl, bs_log2, Hkv, kvh, D) + grp * 8;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) buf.k[t4][kk] = load_stream(k_cache + off + kk * 32);
+      }
+#pragma unroll
+      for (int it = 0; it < VIT; ++it) {
+        const int tl = min(it * TPI + v_sub, last);
+        buf.v[it] = load_stream(
+            v_cache + token_row(__shfl(te, tl, 64), tok0 + tl, bs_log2, Hkv, kvh, D) +
+            v_chunk * 8);
+      }
+    }
+  };
+
+  // running softmax state of the current segment: rows r = head 4*grp + r
+  float m_r[RR], l_r[RR];
+  float o[GP][8];
+  auto reset = [&]() {
+#pragma unroll
+    for (int r = 0; r < RR; ++r) {
+      m_r[r] = -INFINITY;
+      l_r[r] = 0.f;
+    }
+#pragma unroll
+    for (int h = 0; h < GP; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
+  };
+  reset();
+  bool first_segment = true;  // the worker's first segment takes partial slot 2w
+  int seg_k0 = cur.k;         // chunk at which the current segment started
+
+  // one chunk into the running state (no memory writes besides the wave's LDS tile)
+  auto accumulate = [&](const Cursor& x, const Buf& buf) {
+    const int valid = x.L - x.k * CH;  // tokens of the chunk inside the context
+    const int kvh = n_hg == 1 ? x.j : x.j / n_hg;
+    const int hg = x.j - kvh * n_hg;
+    const int nh = min(GP, G - hg * GP);
+    // ---- scores: S[head 4*grp + r][token 16*t4 + row] in acc[t4][r]
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
+    f32x4_t acc[T16];
+#pragma unroll
+    for (int t4 = 0; t4 < T16; ++t4) {
       acc[t4] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
         acc[t4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            qa[kk], __builtin_bit_cast(bf16x8_t, kb[t4][kk]), acc[t4], 0, 0, 0);
+            __builtin_bit_cast(bf16x8_t, row < nh ? buf.q[kk] : zero),
+            __builtin_bit_cast(bf16x8_t, buf.k[t4][kk]), acc[t4], 0, 0, 0);
     }
-
     // ---- online softmax (log2 domain), per head row
-    float alpha_r[4];
+    float alpha_r[RR];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int r = 0; r < RR; ++r) {
       float mx = -INFINITY;
 #pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4) {
-        const float s = (base + 16 * t4 + row < L) ? acc[t4][r] * scale_log2 : -INFINITY;
+      for (int t4 = 0; t4 < T16; ++t4) {
+        const float s = (16 * t4 + row < valid) ? acc[t4][r] * scale_log2 : -INFINITY;
         acc[t4][r] = s;
         mx = fmaxf(mx, s);
       }
-      const float m_new = fmaxf(m_r[r], row16_max(mx));  // finite: token `base` is valid
-      alpha_r[r] = exp2f(m_r[r] - m_new);
+      const float m_new = fmaxf(m_r[r], row16_max(mx));  // finite: the chunk's row 0 is valid
+      alpha_r[r] = __builtin_amdgcn_exp2f(m_r[r] - m_new);
       float sum = 0.f;
 #pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4) {
-        const float p = exp2f(acc[t4][r] - m_new);
+      for (int t4 = 0; t4 < T16; ++t4) {
+        const float p = __builtin_amdgcn_exp2f(acc[t4][r] - m_new);
         acc[t4][r] = p;
         sum += p;
       }
@@ -207,7 +354,7 @@ __global__ __launch_bounds__(256, 2) void paged_decode_bf16_kernel(
       m_r[r] = m_new;
     }
 #pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4)
+    for (int t4 = 0; t4 < T16; ++t4)
       *reinterpret_cast<f32x4_t*>(&p_lds[wave][16 * t4 + row][4 * grp]) = acc[t4];
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -228,7 +375,10 @@ __global__ __launch_bounds__(256, 2) void paged_decode_bf16_kernel(
 #pragma unroll
         for (int h4 = 0; h4 < GP; h4 += 4) {
           const f32x4_t pv = *reinterpret_cast<const f32x4_t*>(&p_lds[wave][tl][h4]);
-          p[h4] = pv[0]; p[h4 + 1] = pv[1]; p[h4 + 2] = pv[2]; p[h4 + 3] = pv[3];
+          p[h4] = pv[0];
+          p[h4 + 1] = pv[1];
+          p[h4 + 2] = pv[2];
+          p[h4 + 3] = pv[3];
         }
       } else {
 #pragma unroll
@@ -237,168 +387,294 @@ __global__ __launch_bounds__(256, 2) void paged_decode_bf16_kernel(
       float v[8];
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        v[2 * w] = bf16_lo(vb[it][w]);
-        v[2 * w + 1] = bf16_hi(vb[it][w]);
+        v[2 * w] = bf16_lo(buf.v[it][w]);
+        v[2 * w + 1] = bf16_hi(buf.v[it][w]);
       }
 #pragma unroll
       for (int h = 0; h < GP; ++h)
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[h][e] += p[h] * v[e];
     }
-    // p_lds[wave] is rewritten next iteration: keep this wave's reads before those writes
+    // p_lds[wave] is rewritten by the next chunk: keep these reads before those writes
     __builtin_amdgcn_wave_barrier();
-  }
+  };
 
-  // ---- merge lanes of the wave: sums over the token sub-groups of each chunk
-#pragma unroll
-  for (int h = 0; h < GP; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float x = o[h][e];
-#pragma unroll
-      for (int sft = DCH; sft < 64; sft <<= 1) x += __shfl_xor(x, sft, 64);
-      o[h][e] = x;
-    }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) l_r[r] = row16_sum(l_r[r]);
-  if (row == 0) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      m_lds[wave][4 * grp + r] = m_r[r];
-      l_lds[wave][4 * grp + r] = l_r[r];
-    }
-  }
-  if (v_sub == 0) {
+  // End of a segment (x is its last chunk): the final output if the whole stream ran
+  // on this worker, else the worker's partial for the combine kernel.
+  auto finalize = [&](const Cursor& x) {
+    const int kvh = n_hg == 1 ? x.j : x.j / n_hg;
+    const int hg = x.j - kvh * n_hg;
+    const int nh = min(GP, G - hg * GP);
+    // reduce over the lanes sharing a head_dim piece
 #pragma unroll
     for (int h = 0; h < GP; ++h)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o_lds[wave][h][v_chunk * 8 + e] = o[h][e];
-  }
-  __syncthreads();
+      for (int e = 0; e < 8; ++e) {
+        float t = o[h][e];
+#pragma unroll
+        for (int sft = DCH; sft < 64; sft <<= 1) t += __shfl_xor(t, sft, 64);
+        o[h][e] = t;
+      }
+    float l_h[GP], m_h[GP];
+#pragma unroll
+    for (int r = 0; r < RR; ++r) l_r[r] = row16_sum(l_r[r]);
+#pragma unroll
+    for (int h = 0; h < GP; ++h) {
+      l_h[h] = read_lane(l_r[h & 3], 16 * (h >> 2));
+      m_h[h] = read_lane(m_r[h & 3], 16 * (h >> 2));
+    }
+    const int64_t hq0 = static_cast<int64_t>(x.b) * Hq + kvh * G + hg * GP;
+    if (seg_k0 == 0 && x.k == x.nch - 1) {
+      // the whole stream ran here: final output
+      if (v_sub == 0) {
+#pragma unroll
+        for (int h = 0; h < GP; ++h) {
+          if (h >= nh) break;
+          const float inv = 1.f / l_h[h];
+          u32x4_t w;
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2)
+            w[e2] = pack_bf16x2(o[h][2 * e2] * inv, o[h][2 * e2 + 1] * inv);
+          *reinterpret_cast<u32x4_t*>(out + (hq0 + h) * D + v_chunk * 8) = w;
+        }
+      }
+    } else {
+      const int64_t slot = 2 * static_cast<int64_t>(worker) + (first_segment ? 0 : 1);
+      if (v_sub == 0) {
+#pragma unroll
+        for (int h = 0; h < GP; ++h) {
+          float* dst = ws_o + (slot * GP + h) * D + v_chunk * 8;
+          *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{o[h][0], o[h][1], o[h][2], o[h][3]};
+          *reinterpret_cast<f32x4_t*>(dst + 4) = f32x4_t{o[h][4], o[h][5], o[h][6], o[h][7]};
+        }
+      }
+      if (lane < GP) {
+        float mm = m_h[0], ll = l_h[0];
+#pragma unroll
+        for (int h = 1; h < GP; ++h)
+          if (lane == h) {
+            mm = m_h[h];
+            ll = l_h[h];
+          }
+        ws_ml[slot * GP + lane] = make_float2(mm, ll);
+      }
+    }
+    reset();
+    first_segment = false;
+  };
 
-  // ---- merge the four waves exactly, then write the output or the split's partial
-  for (int idx = threadIdx.x; idx < nh * D; idx += 256) {
+  // ---- the pipelined walk: chunk i computes while chunk i+1 loads and the table
+  // entry of chunk i+2 is fetched.  The chunk after the worker's last is a dummy.
+  // The inner loop runs the chunks of one segment and holds no global store (a store
+  // there would make the next chunk's register reuse wait for every load in flight);
+  // segment ends are finalized in the outer loop.  32-bit counters: a 64-bit compare
+  // of uniform values would borrow a vector register and wait the same way.
+  const int n_chunks = static_cast<int>(c_end - c_begin);
+  Buf bufA, bufB;
+  int i = 0;
+  Cursor nxt = cur;
+  if (n_chunks > 1) advance(nxt);
+  int te_nxt = table_entry(nxt);
+  issue(cur, table_entry(cur), bufA, true);
+  bool has_next = false;
+  Cursor nn = nxt;
+  int te_nn = 0;
+  // Process `cur` from X after issuing `nxt` into Y; true at a segment end (the
+  // cursors then advance after the finalize).
+  auto step = [&](Buf& X, Buf& Y) -> bool {
+    has_next = i + 1 < n_chunks;
+    nn = nxt;
+    if (i + 2 < n_chunks) advance(nn);
+    te_nn = table_entry(nn);
+    issue(nxt, te_nxt, Y, has_next);
+    // keep those loads here, ahead of the computation of the current chunk
+    __builtin_amdgcn_sched_barrier(0);
+    accumulate(cur, X);
+    if (!has_next || cur.k == cur.nch - 1) return true;
+    ++i;
+    cur = nxt;
+    nxt = nn;
+    te_nxt = te_nn;
+    return false;
+  };
+  // The two half-steps appear once each; a segment that starts with its chunk in
+  // bufB enters the loop at the second one.
+  bool start_in_b = false;
+  for (;;) {
+    bool ended_in_a;
+    for (;;) {
+      if (!start_in_b && step(bufA, bufB)) {
+        ended_in_a = true;
+        break;
+      }
+      start_in_b = false;
+      if (step(bufB, bufA)) {
+        ended_in_a = false;
+        break;
+      }
+    }
+    finalize(cur);
+    if (!has_next) break;
+    start_in_b = ended_in_a;  // the next chunk sits in the other buffer
+    ++i;
+    cur = nxt;
+    nxt = nn;
+    te_nxt = te_nn;
+    seg_k0 = 0;
+  }
+}
+
+// Merge of the per-worker partials of every stream that was cut between workers.
+// Grid: (stream within sequence, sequence).
+template <int D, int GP, int CH>
+__global__ __launch_bounds__(128) void decode_combine_kernel(
+    const int64_t* __restrict__ ws_prefix, const float2* __restrict__ ws_ml,
+    const float* __restrict__ ws_o, uint16_t* __restrict__ out,
+    const int32_t* __restrict__ context_lens, int batch, int Hq, int G, int n_hg,
+    int num_workers) {
+  const int j = blockIdx.x;
+  const int b = blockIdx.y;
+  const int nch = chunks_of<CH>(context_lens[b]);
+  if (nch == 0) return;
+  const int64_t C = ws_prefix[batch];
+  const int64_t W = num_workers;
+  const int64_t cs = ws_prefix[b] + static_cast<int64_t>(j) * nch;
+  const int64_t ce = cs + nch - 1;
+  const int64_t wa = worker_of(cs, C, W);
+  const int64_t wb = worker_of(ce, C, W);
+  if (wa == wb) return;  // finished by one worker
+  const int kvh = j / n_hg;
+  const int hg = j - kvh * n_hg;
+  const int nh = min(GP, G - hg * GP);
+  const int64_t hq0 = static_cast<int64_t>(b) * Hq + kvh * G + hg * GP;
+  const bool wa_second = wa * C / W < cs;  // worker wa had an earlier segment
+  for (int idx = threadIdx.x; idx < nh * D; idx += blockDim.x) {
     const int h = idx / D;
     const int d = idx - h * D;
     float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, m_lds[w][h]);
+    for (int64_t w = wa; w <= wb; ++w) {
+      if (w > wa && w * C / W == (w + 1) * C / W) continue;  // empty range
+      const int64_t slot = 2 * w + (w == wa && wa_second ? 1 : 0);
+      M = fmaxf(M, ws_ml[slot * GP + h].x);
+    }
     float lsum = 0.f, osum = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float f = exp2f(m_lds[w][h] - M);  // 0 for a wave without tokens
-      lsum += f * l_lds[w][h];
-      osum += f * o_lds[w][h][d];
+    for (int64_t w = wa; w <= wb; ++w) {
+      if (w > wa && w * C / W == (w + 1) * C / W) continue;
+      const int64_t slot = 2 * w + (w == wa && wa_second ? 1 : 0);
+      const float2 ml = ws_ml[slot * GP + h];
+      const float f = exp2f(ml.x - M);
+      lsum += f * ml.y;
+      osum += f * ws_o[(slot * GP + h) * D + d];
     }
-    const int64_t hq = static_cast<int64_t>(b) * Hq + h0 + h;
-    if (n_splits == 1) {
-      out[hq * D + d] = static_cast<uint16_t>(f32_to_bf16_bits(osum / lsum));
-    } else {
-      ws_o[(hq * max_splits + split) * D + d] = osum;
-      if (d == 0) ws_ml[hq * max_splits + split] = make_float2(M, lsum);
-    }
+    out[(hq0 + h) * D + d] = static_cast<uint16_t>(f32_to_bf16_bits(osum / lsum));
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void decode_combine_kernel(
-    const float* __restrict__ ws_o, const float2* __restrict__ ws_ml, uint16_t* __restrict__ out,
-    const int32_t* __restrict__ context_lens, int Hq, int split_tokens, int max_splits) {
-  const int b = blockIdx.y;
-  const int idx = blockIdx.x * 256 + threadIdx.x;
-  if (idx >= Hq * D) return;
-  const int L = context_lens[b];
-  const int n = (L + split_tokens - 1) / split_tokens;
-  if (n <= 1) return;  // written directly by the split kernel
-  const int h = idx / D;
-  const int d = idx - h * D;
-  const int64_t hq = static_cast<int64_t>(b) * Hq + h;
-  const float2* ml = ws_ml + hq * max_splits;
-  float M = -INFINITY;
-  for (int s = 0; s < n; ++s) M = fmaxf(M, ml[s].x);
-  float lsum = 0.f, osum = 0.f;
-  for (int s = 0; s < n; ++s) {
-    const float f = exp2f(ml[s].x - M);
-    lsum += f * ml[s].y;
-    osum += f * ws_o[(hq * max_splits + s) * D + d];
+namespace {
+
+int heads_per_stream(int G) { return G >= 8 ? 8 : (G >= 4 ? 4 : (G >= 2 ? 2 : 1)); }
+
+constexpr int kMaxAutoWorkers = 4096;
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+template <int D, int GP, int CH, bool ONE_BLOCK>
+int auto_workers() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int w = cached[dev].load(std::memory_order_relaxed);
+  if (w > 0) return w;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &per_cu, reinterpret_cast<const void*>(&paged_decode_bf16_kernel<D, GP, CH, ONE_BLOCK>), 256, 0) !=
+          hipSuccess ||
+      cus <= 0 || per_cu <= 0) {
+    cus = 256;
+    per_cu = 2;
   }
-  out[hq * D + d] = static_cast<uint16_t>(f32_to_bf16_bits(osum / lsum));
+  w = std::min(kMaxAutoWorkers, cus * per_cu * 4);
+  cached[dev].store(w, std::memory_order_relaxed);
+  return w;
 }
 
-void decode_split_plan(int max_context_len, int num_splits, int* split_tokens,
-                       int* max_splits) {
-  const int chunks = (max_context_len + 255) / 256;
-  const int per = num_splits > 0 ? (chunks + num_splits - 1) / num_splits : 1;
-  *split_tokens = per * 256;
-  *max_splits = (max_context_len + *split_tokens - 1) / *split_tokens;
+template <int D, int GP, int CH, bool ONE_BLOCK>
+hipError_t launch_decode(const void* q, void* out, const void* k_cache, const void* v_cache,
+                         int num_q_heads, int num_kv_heads, int bs_log2, int batch,
+                         const int32_t* context_lens, const int32_t* block_tables,
+                         int table_stride, float scale, int num_workers, void* workspace,
+                         hipStream_t stream) {
+  const int G = num_q_heads / num_kv_heads;
+  const int n_hg = (G + GP - 1) / GP;
+  const int S = num_kv_heads * n_hg;
+  if (S > 65535) return hipErrorInvalidConfiguration;
+  const int W = num_workers > 0 ? num_workers : auto_workers<D, GP, CH, ONE_BLOCK>();
+  int64_t* ws_prefix = static_cast<int64_t*>(workspace);
+  char* base = static_cast<char*>(workspace) + align256(sizeof(int64_t) * (batch + 1));
+  float2* ws_ml = reinterpret_cast<float2*>(base);
+  float* ws_o = reinterpret_cast<float*>(base + align256(sizeof(float2) * 2 * W * GP));
+  const float scale_log2 = scale * kLog2e;
+  timing_begin("paged_decode", stream);
+  hipLaunchKernelGGL((paged_decode_bf16_kernel<D, GP, CH, ONE_BLOCK>), dim3((W + 3) / 4), dim3(256), 0,
+                     stream, static_cast<const uint16_t*>(q), static_cast<uint16_t*>(out),
+                     static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache),
+                     context_lens, block_tables, table_stride, batch, num_q_heads, num_kv_heads,
+                     G, n_hg, bs_log2, scale_log2, W, ws_prefix, ws_ml, ws_o);
+  timing_end(stream);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  timing_begin("paged_decode_combine", stream);
+  hipLaunchKernelGGL((decode_combine_kernel<D, GP, CH>), dim3(S, batch), dim3(128), 0, stream,
+                     ws_prefix, ws_ml, ws_o, static_cast<uint16_t*>(out), context_lens, batch,
+                     num_q_heads, G, n_hg, W);
+  timing_end(stream);
+  return hipGetLastError();
 }
 
-template <int D, int GP>
-static void launch_split(dim3 grid, hipStream_t stream, const uint16_t* q, uint16_t* out,
-                         const uint16_t* kc, const uint16_t* vc, const int32_t* ctx,
-                         const int32_t* tables, int stride, int Hq, int Hkv, int G, int n_hg,
-                         int bs_log2, int split_tokens, int max_splits, float scale_log2,
-                         float* ws_o, float2* ws_ml) {
-  hipLaunchKernelGGL((paged_decode_bf16_kernel<D, GP>), grid, dim3(256), 0, stream, q, out, kc,
-                     vc, ctx, tables, stride, Hq, Hkv, G, n_hg, bs_log2, split_tokens, max_splits,
-                     scale_log2, ws_o, ws_ml);
+}  // namespace
+
+size_t paged_decode_bf16_workspace(int head_dim, int num_q_heads, int num_kv_heads, int batch,
+                                   int num_workers) {
+  const int GP = heads_per_stream(num_q_heads / num_kv_heads);
+  const size_t W = num_workers > 0 ? static_cast<size_t>(num_workers) : kMaxAutoWorkers;
+  return align256(sizeof(int64_t) * (static_cast<size_t>(batch) + 1)) +
+         align256(sizeof(float2) * 2 * W * GP) + sizeof(float) * 2 * W * GP * head_dim;
 }
 
 hipError_t launch_paged_decode_bf16(int head_dim, const void* q, void* out, const void* k_cache,
                                     const void* v_cache, int num_q_heads, int num_kv_heads,
                                     int bs_log2, int batch, const int32_t* context_lens,
                                     const int32_t* block_tables, int table_stride, float scale,
-                                    int split_tokens, int max_splits, void* workspace,
-                                    hipStream_t stream) {
-  const int G = num_q_heads / num_kv_heads;
-  const int GP = G >= 8 ? 8 : (G >= 4 ? 4 : (G >= 2 ? 2 : 1));
-  const int n_hg = (G + GP - 1) / GP;
-  if (num_kv_heads * n_hg > 65535) return hipErrorInvalidConfiguration;
-  const float scale_log2 = scale * kLog2e;
-  float* ws_o = static_cast<float*>(workspace);
-  float2* ws_ml = nullptr;
-  if (max_splits > 1)
-    ws_ml = reinterpret_cast<float2*>(ws_o + static_cast<int64_t>(batch) * num_q_heads *
-                                                 max_splits * head_dim);
-  const dim3 grid(max_splits, num_kv_heads * n_hg, batch);
-  auto qq = static_cast<const uint16_t*>(q);
-  auto oo = static_cast<uint16_t*>(out);
-  auto kc = static_cast<const uint16_t*>(k_cache);
-  auto vc = static_cast<const uint16_t*>(v_cache);
-#define PKV_SPLIT(D_, GP_)                                                                   \
-  launch_split<D_, GP_>(grid, stream, qq, oo, kc, vc, context_lens, block_tables,            \
-                        table_stride, num_q_heads, num_kv_heads, G, n_hg, bs_log2,           \
-                        split_tokens, max_splits, scale_log2, ws_o, ws_ml)
-  timing_begin("paged_decode_split", stream);
+                                    int num_workers, void* workspace, hipStream_t stream) {
+  // 16-token chunks: two of them in flight per wave keep enough bytes outstanding
+  // while leaving registers for several waves per SIMD
+  const int GP = heads_per_stream(num_q_heads / num_kv_heads);
+#define PKV_DEC(D_, GP_, CH_)                                                                \
+  return bs_log2 >= 4                                                                        \
+             ? launch_decode<D_, GP_, CH_, true>(q, out, k_cache, v_cache, num_q_heads,     \
+                                                 num_kv_heads, bs_log2, batch, context_lens, \
+                                                 block_tables, table_stride, scale,          \
+                                                 num_workers, workspace, stream)             \
+             : launch_decode<D_, GP_, CH_, false>(q, out, k_cache, v_cache, num_q_heads,    \
+                                                  num_kv_heads, bs_log2, batch, context_lens, \
+                                                  block_tables, table_stride, scale,         \
+                                                  num_workers, workspace, stream)
   if (head_dim == 128) {
     switch (GP) {
-      case 1: PKV_SPLIT(128, 1); break;
-      case 2: PKV_SPLIT(128, 2); break;
-      case 4: PKV_SPLIT(128, 4); break;
-      default: PKV_SPLIT(128, 8); break;
-    }
-  } else {
-    switch (GP) {
-      case 1: PKV_SPLIT(64, 1); break;
-      case 2: PKV_SPLIT(64, 2); break;
-      case 4: PKV_SPLIT(64, 4); break;
-      default: PKV_SPLIT(64, 8); break;
+      case 1: PKV_DEC(128, 1, 16);
+      case 2: PKV_DEC(128, 2, 16);
+      case 4: PKV_DEC(128, 4, 16);
+      default: PKV_DEC(128, 8, 16);
     }
   }
-#undef PKV_SPLIT
-  timing_end(stream);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || max_splits <= 1) return e;
-  const dim3 cgrid((num_q_heads * head_dim + 255) / 256, batch);
-  timing_begin("paged_decode_combine", stream);
-  if (head_dim == 128)
-    hipLaunchKernelGGL(decode_combine_kernel<128>, cgrid, dim3(256), 0, stream, ws_o, ws_ml, oo,
-                       context_lens, num_q_heads, split_tokens, max_splits);
-  else
-    hipLaunchKernelGGL(decode_combine_kernel<64>, cgrid, dim3(256), 0, stream, ws_o, ws_ml, oo,
-                       context_lens, num_q_heads, split_tokens, max_splits);
-  timing_end(stream);
-  return hipGetLastError();
+  switch (GP) {
+    case 1: PKV_DEC(64, 1, 16);
+    case 2: PKV_DEC(64, 2, 16);
+    case 4: PKV_DEC(64, 4, 16);
+    default: PKV_DEC(64, 8, 16);
+  }
+#undef PKV_DEC
 }
 
 }  // namespace pkv

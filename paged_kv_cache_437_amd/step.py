@@ -44,10 +44,10 @@ def _fill_bits(t: torch.Tensor, bits: int) -> None:
 
 class DeviceStep:
     def __init__(self, wl, device="cuda", stale: str | None = "nan", table_pad: int = -1,
-                 num_splits: int = 0, plan=None):
+                 num_workers: int = 0, plan=None):
         self.wl = wl
         self.device = torch.device(device)
-        self.num_splits = num_splits
+        self.num_workers = num_workers
         pool = BlockPool(wl.num_blocks, wl.free_order)
         self.plan = plan if plan is not None else plan_step(wl.seqs, wl.block_size, pool,
                                                             table_pad)
@@ -99,7 +99,7 @@ class DeviceStep:
             self.decode_tables = i32(p.decode_block_tables)
             self.out_decode = torch.empty_like(self.q_decode)
             ws = paged_decode_workspace_size(self.k_cache, self.v_cache, wl.num_q_heads,
-                                             len(p.decode), p.max_context_len, num_splits)
+                                             len(p.decode), p.max_context_len, num_workers)
             self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
 
     # the three calls of the hot path, separately (for per-kernel timing) and together
@@ -120,7 +120,7 @@ class DeviceStep:
         p = self.plan
         return paged_decode(self.q_decode, self.k_cache, self.v_cache, self.decode_tables,
                             self.context_lens, p.max_context_len, self.wl.scale,
-                            num_splits=self.num_splits, out=self.out_decode,
+                            num_workers=self.num_workers, out=self.out_decode,
                             workspace=self.workspace)
 
     def run(self):

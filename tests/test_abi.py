@@ -65,9 +65,9 @@ def prefill(lib, c, hq=4, batch=1, max_q=8, max_k=8, stride=1, tables=FAKE):
                                         max_q, max_k, tables, stride, 0.125, None)
 
 
-def decode(lib, c, hq=4, batch=1, max_ctx=64, stride=4, ws=None, ws_bytes=0, splits=0):
+def decode(lib, c, hq=4, batch=1, max_ctx=64, stride=4, ws=None, ws_bytes=0, workers=0):
     return lib.load().pkv_paged_decode(ctypes.byref(c), FAKE, FAKE, hq, batch, FAKE, max_ctx,
-                                       FAKE, stride, 0.125, ws, ws_bytes, splits, None)
+                                       FAKE, stride, 0.125, ws, ws_bytes, workers, None)
 
 
 def test_store_validation(lib):
@@ -102,11 +102,13 @@ def test_decode_validation(lib):
     assert decode(lib, cache(lib), hq=5) == lib.PKV_ERR_INVALID
     assert decode(lib, cache(lib), max_ctx=0) == lib.PKV_ERR_INVALID
     assert decode(lib, cache(lib), max_ctx=65, stride=4) == lib.PKV_ERR_INVALID
-    assert decode(lib, cache(lib), splits=-1) == lib.PKV_ERR_INVALID
+    assert decode(lib, cache(lib), workers=-1) == lib.PKV_ERR_INVALID
+    assert decode(lib, cache(lib), workers=(1 << 20) + 1) == lib.PKV_ERR_INVALID
     assert decode(lib, cache(lib, block_size=3)) == lib.PKV_ERR_UNSUPPORTED
     assert decode(lib, cache(lib), batch=0) == lib.PKV_OK
     c = cache(lib)
     need = lib.load().pkv_paged_decode_workspace_size(ctypes.byref(c), 4, 8, 4096, 0)
+    assert need > 0  # bf16 always needs one (the chunk prefix and the partials)
     if need > 0:
         assert decode(lib, c, batch=8, max_ctx=4096, stride=256) == lib.PKV_ERR_WORKSPACE
         assert decode(lib, c, batch=8, max_ctx=4096, stride=256, ws=FAKE,

@@ -74,7 +74,7 @@ def test_config_parity_more_seeds(pkv, seed):
 
 def test_decode_large_full_size_sampled(pkv):
     """Large decode batch with the pool at 60% of free device memory, in the
-    launch configuration the bench times (automatic splits); 64 sequences
+    launch configuration the bench times (automatic worker count); 64 sequences
     spanning the length range are checked against the oracle one by one."""
     free, _ = torch.cuda.mem_get_info()
     bb = workloads.block_bytes(256, 8, 128, 2)
@@ -158,11 +158,15 @@ def test_rerun_deterministic(pkv):
     assert np.array_equal(a["decode"], b["decode"])
 
 
-@pytest.mark.parametrize("splits", [1, 2, 3, 7])
-def test_split_count_agrees(pkv, splits):
-    wl = workloads.decode_large(seed=8, batch=24)
-    ref = oracle.run_step(wl)
-    _check_outputs(wl, _step(wl, num_splits=splits), ref)
+@pytest.mark.parametrize("workers", [1, 2, 3, 7, 61, 1000])
+def test_worker_count_agrees(pkv, workers):
+    """Any division of the chunk list among workers (1 = every stream whole on one
+    worker; more workers than chunks = idle workers) merges to the oracle's result:
+    GQA 4 with 256-token blocks, MHA head_dim 64 with 4-token blocks (the per-lane
+    block path), and 16 q heads per kv head (two head groups per stream)."""
+    for wl in (workloads.decode_large(seed=8, batch=24), edge_workloads(3)[1],
+               edge_workloads(3)[6]):
+        _check_outputs(wl, _step(wl, num_workers=workers), oracle.run_step(wl))
 
 
 def test_decode_equals_last_prefill_row(pkv):
