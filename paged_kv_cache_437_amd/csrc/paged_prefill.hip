@@ -38,6 +38,9 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
+// (1, 1) in bf16: v_dot2 with it adds a pair of bf16 values into an fp32 sum
+constexpr bf16x2_t kOnes = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+
 __device__ __forceinline__ i16x4_t lds_read_tr16(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) i16x4_t*)(
@@ -45,7 +48,7 @@ __device__ __forceinline__ i16x4_t lds_read_tr16(const uint16_t* p) {
               reinterpret_cast<uintptr_t>(p))));
 }
 
-template <int D, int GP>
+template <int D, int GP, bool BIG_BLOCK>
 __global__ __launch_bounds__(256, 2) void paged_prefill_bf16_kernel(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
     const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
@@ -61,6 +64,10 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_bf16_kernel(
   constexpr int CPR = D / 8;        // 16-byte chunks per K/V row
   constexpr int RPI = 256 / CPR;    // rows per workgroup load instruction
   constexpr int LIT = BN / RPI;     // load instructions per tile (K and V each)
+  // Lazy rescaling: the running max a row's probabilities are taken against moves
+  // only when a new score exceeds it by more than 2^8 (log2 domain), so most tiles
+  // skip the rescale of the accumulators; probabilities stay <= 2^8.
+  constexpr float kRescaleSlack = 8.f;
 
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][BN][KP];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][BN][KP];
@@ -82,6 +89,7 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_bf16_kernel(
   const int tok0 = tile * BM_TOK;
   const int32_t* table = block_tables + static_cast<int64_t>(b) * table_stride;
   const int bs_mask = (1 << bs_log2) - 1;
+  const uint32_t row_bytes = static_cast<uint32_t>(Hkv) * D * 2;  // token stride in a block
 
   // this lane's query row (rows are head-major: 32 rows of a wave share a head when GP<=4)
   const int R = 32 * wave + l32;
@@ -108,40 +116,40 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_bf16_kernel(
   const int n_kv = (k_end + BN - 1) / BN;
   const int first_masked_tile = (Lk - Lq + tok0) / BN;  // tiles before it need no mask
 
-  // global -> register staging of one K/V tile
+  // ---- global -> register staging of one K/V tile.  Every load is unconditional:
+  // keys at or past Lk re-read the tile's last valid key (real data, never stale
+  // memory); their scores are masked and their probabilities are 0.
   const int ld_row = tid / CPR;
   const int ld_chunk = tid - ld_row * CPR;
   u32x4_t kst[LIT], vst[LIT];
-  auto fetch = [&](int t) {
+  // block id of tile t (a vector load so it counts in order with the K/V loads;
+  // with BIG_BLOCK a 64-key tile lies in one block and every lane gets the same id)
+  auto tile_block = [&](int t) -> int {
+    return table[min(t * BN + (lane & (BN - 1)), Lk - 1) >> bs_log2];
+  };
+  auto fetch = [&](int t, int te) {
     const int kv0 = t * BN;
-    if (bs_log2 >= 6) {
-      const int64_t blk = table[kv0 >> bs_log2];
+    const int last = min(Lk - kv0, BN) - 1;
+    if constexpr (BIG_BLOCK) {
+      const int64_t blk = __builtin_amdgcn_readfirstlane(te);
+      const int64_t first = (((blk << bs_log2) | (kv0 & bs_mask)) * Hkv + kvh) * D;
+      const char* kb = reinterpret_cast<const char*>(k_cache + first);
+      const char* vb = reinterpret_cast<const char*>(v_cache + first);
 #pragma unroll
       for (int it = 0; it < LIT; ++it) {
-        const int key = kv0 + it * RPI + ld_row;
-        u32x4_t kw = {0u, 0u, 0u, 0u}, vw = {0u, 0u, 0u, 0u};
-        if (key < Lk) {
-          const int64_t off =
-              (((blk << bs_log2) | (key & bs_mask)) * Hkv + kvh) * D + ld_chunk * 8;
-          kw = *reinterpret_cast<const u32x4_t*>(k_cache + off);
-          vw = *reinterpret_cast<const u32x4_t*>(v_cache + off);
-        }
-        kst[it] = kw;
-        vst[it] = vw;
+        const uint32_t off =
+            static_cast<uint32_t>(min(it * RPI + ld_row, last)) * row_bytes + ld_chunk * 16;
+        kst[it] = *reinterpret_cast<const u32x4_t*>(kb + off);
+        vst[it] = *reinterpret_cast<const u32x4_t*>(vb + off);
       }
     } else {
 #pragma unroll
       for (int it = 0; it < LIT; ++it) {
-        const int key = kv0 + it * RPI + ld_row;
-        u32x4_t kw = {0u, 0u, 0u, 0u}, vw = {0u, 0u, 0u, 0u};
-        if (key < Lk) {
-          const int64_t off =
-              token_row(table[key >> bs_log2], key, bs_log2, Hkv, kvh, D) + ld_chunk * 8;
-          kw = *reinterpret_cast<const u32x4_t*>(k_cache + off);
-          vw = *reinterpret_cast<const u32x4_t*>(v_cache + off);
-        }
-        kst[it] = kw;
-        vst[it] = vw;
+        const int key = kv0 + min(it * RPI + ld_row, last);
+        const int64_t off =
+            token_row(table[key >> bs_log2], key, bs_log2, Hkv, kvh, D) + ld_chunk * 8;
+        kst[it] = *reinterpret_cast<const u32x4_t*>(k_cache + off);
+        vst[it] = *reinterpret_cast<const u32x4_t*>(v_cache + off);
       }
     }
   };
@@ -158,16 +166,26 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_bf16_kernel(
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
-  float m = -INFINITY;  // running max of raw scores of this row
-  float l = 0.f;        // this lane's share of the running sum
+  float m = -INFINITY;  // reference max of this row, scaled to the log2 domain
+  float l = 0.f;        // this lane's share of the row's sum of (bf16-rounded) probabilities
 
-  fetch(0);
+  int te_next = BIG_BLOCK ? tile_block(0) : 0;
+  fetch(0, te_next);
+  if (BIG_BLOCK && n_kv > 1) te_next = tile_block(1);
   stage(0);
   __syncthreads();
 
   for (int t = 0; t < n_kv; ++t) {
     const int buf = t & 1;
-    if (t + 1 < n_kv) fetch(t + 1);
+    const bool has_next = t + 1 < n_kv;
+    // the next tile's loads go out first and land while this tile is computed
+    if (has_next) {
+      fetch(t + 1, te_next);
+      // the entry after it reuses te_next's register: it is fetched only once the
+      // K/V loads have consumed the old value
+      if (BIG_BLOCK) te_next = tile_block(min(t + 2, n_kv - 1));
+    }
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- S^T = K Q^T for 64 keys: s[sub][r] is key 32*sub + 8*(r/4) + 4*hi + r%4
     f32x16_t s[2];
@@ -195,18 +213,24 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_bf16_kernel(
         }
     }
 
-    // ---- online softmax: row max over this lane's 32 keys and lane^32's
+    // ---- online softmax in the log2 domain; the row max is this lane's 32 keys and
+    // lane^32's
     float mx = s[0][0];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sub][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m, mx);  // finite: key 0 of tile 0 is visible to every row
-    const float alpha = exp2f((m - m_new) * scale_log2);
-    const float mc = m_new * scale_log2;
-    m = m_new;
-    float psum = 0.f;
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
+    if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleSlack)) {  // wavefront-uniform
+      const float m_new = fmaxf(m, mx);  // finite: key 0 of tile 0 is visible to every row
+      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+      m = m_new;
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+    }
     bf16x8_t pb[4];  // P^T operand of k-step ks = 2*sub + half
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
@@ -215,18 +239,18 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_bf16_kernel(
         u32x4_t w;
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
-          const float p0 = exp2f(s[sub][8 * half + 2 * e2] * scale_log2 - mc);
-          const float p1 = exp2f(s[sub][8 * half + 2 * e2 + 1] * scale_log2 - mc);
-          psum += p0 + p1;
-          w[e2] = pack_bf16x2(p0, p1);
+          const float p0 =
+              __builtin_amdgcn_exp2f(__builtin_fmaf(s[sub][8 * half + 2 * e2], scale_log2, -m));
+          const float p1 = __builtin_amdgcn_exp2f(
+              __builtin_fmaf(s[sub][8 * half + 2 * e2 + 1], scale_log2, -m));
+          const bf16x2_t pk = {static_cast<__bf16>(p0), static_cast<__bf16>(p1)};
+          w[e2] = __builtin_bit_cast(uint32_t, pk);
+          // the sum takes the rounded probabilities the P.V product uses (the packed
+          // pair goes to the dot product as its own value, not re-read out of w)
+          l = __builtin_amdgcn_fdot2_f32_bf16(pk, kOnes, l, false);
         }
         pb[2 * sub + half] = __builtin_bit_cast(bf16x8_t, w);
       }
-    l = l * alpha + psum;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
 
     // ---- O^T += V^T P^T: A = V^T via transposing LDS reads, keys in the same order as P
     const int g = lane >> 4;         // 16-lane group
@@ -248,7 +272,7 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_bf16_kernel(
       }
     }
 
-    if (t + 1 < n_kv) stage(buf ^ 1);
+    if (has_next) stage(buf ^ 1);
     __syncthreads();
   }
 
@@ -274,7 +298,10 @@ static void launch_prefill(dim3 grid, hipStream_t stream, const void* q, void* o
                            const void* kc, const void* vc, const int32_t* cu_q,
                            const int32_t* cu_k, const int32_t* tables, int stride, int Hq,
                            int Hkv, int G, int bs_log2, float scale_log2) {
-  hipLaunchKernelGGL((paged_prefill_bf16_kernel<D, GP>), grid, dim3(256), 0, stream,
+  // blocks of at least 64 tokens hold a whole 64-key tile
+  auto kernel = bs_log2 >= 6 ? paged_prefill_bf16_kernel<D, GP, true>
+                             : paged_prefill_bf16_kernel<D, GP, false>;
+  hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<uint16_t*>(out),
                      static_cast<const uint16_t*>(kc), static_cast<const uint16_t*>(vc), cu_q,
                      cu_k, tables, stride, Hq, Hkv, G, bs_log2, scale_log2);
