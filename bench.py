@@ -48,6 +48,9 @@ def parse():
                     help="time only the prefill leg (for profiling it alone)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="rough CPU budget of the oracle baseline sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only copy 1 GiB device to device 5 times (a plain copy kernel of "
+                         "known size, to scale HBM byte counters against)")
     return ap.parse_args()
 
 
@@ -185,6 +188,19 @@ def main():
         from paged_kv_cache_437_amd.build import build
         build()
     _lib.load()
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration": {"bytes_read_per_copy": n,
+                                               "bytes_written_per_copy": n, "copies": 5}}),
+              flush=True)
+        return
 
     if args.prefill_only:
         print(json.dumps({"prefill": prefill_leg(torch, pkv, workloads, DeviceStep, args)}),

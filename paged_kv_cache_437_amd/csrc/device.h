@@ -57,6 +57,17 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// Sum of an int over a full wavefront, returned wavefront-uniform: DPP within each
+// row of 16 lanes (quad swaps, half-row and row mirrors), then the four row sums.
+__device__ __forceinline__ int wave_sum_uniform(int x) {
+  x += __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+  x += __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+  x += __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false);  // row_half_mirror
+  x += __builtin_amdgcn_mov_dpp(x, 0x140, 0xF, 0xF, false);  // row_mirror
+  return __builtin_amdgcn_readlane(x, 0) + __builtin_amdgcn_readlane(x, 16) +
+         __builtin_amdgcn_readlane(x, 32) + __builtin_amdgcn_readlane(x, 48);
+}
+
 // Row of token `pos` of a sequence for kv head `kvh`, as an element offset into a
 // [num_blocks][block_size][Hkv][D] cache.  64-bit: large pools exceed 2^31 elements.
 __device__ __forceinline__ int64_t token_row(int32_t block, int pos, int bs_log2, int Hkv,

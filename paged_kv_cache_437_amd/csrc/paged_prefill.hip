@@ -22,12 +22,14 @@
 // so the P registers produced by the S^T MFMA feed the O^T MFMA without shuffles.
 // K/V tiles are double buffered in LDS with rows padded to (D + 16) elements (no
 // bank conflicts for the 16-byte and the transposing reads); tile j+1 is fetched
-// into registers while tile j is computed.  Keys at or past Lk are zero-filled
-// (stale rows never enter), table entries past the last used block are never read,
-// and causal masking is applied only on tiles that cross the diagonal.
-// Work order: blockIdx.x = (sequence, kv head), blockIdx.y = tile rank counted from
-// each sequence's last (heaviest) tile, so long causal tiles start first and the
-// tiles sharing one sequence's K/V land on the same XCD when Hkv * batch % 8 == 0.
+// into registers while tile j is computed.  Keys at or past Lk re-read the tile's
+// last valid key (stale rows never enter; their scores are masked), table entries
+// past the last used block are never read, and causal masking is applied only on
+// tiles that cross the diagonal.
+// Work order: workgroups take the (sequence, kv head, q tile) items by tile rank
+// counted from each sequence's last (heaviest) tile, so long causal tiles start
+// first; the grid is sized for the longest sequence and the slots past the real
+// items (shorter sequences have fewer tiles) come last and exit at once.
 #include "device.h"
 #include "launch.h"
 #include "timing.h"
@@ -48,13 +50,74 @@ __device__ __forceinline__ i16x4_t lds_read_tr16(const uint16_t* p) {
               reinterpret_cast<uintptr_t>(p))));
 }
 
+// Workgroup -> work item.  Item i of the list ordered by q-tile rank counted from
+// each sequence's last (heaviest) tile, rank 0 first, then by (sequence, kv head).
+// With n_b q tiles in sequence b, rank y holds Hkv * #{b : n_b > y} items, so the
+// ranks below y hold P(y) = Hkv * sum_b min(n_b, y) items: a binary search on P
+// finds the rank, a ballot the sequence.  Returns false for i past the list.  Every
+// value is wavefront-uniform.
+__device__ bool prefill_item(int64_t i, int batch, int Hkv, int bm_tok, int max_tiles,
+                             const int32_t* __restrict__ cu_q, int& b_out, int& kvh_out,
+                             int& tile_out) {
+  constexpr int NC = 4;  // chunks of 64 sequences whose tile counts stay in registers
+  const int lane = threadIdx.x & 63;
+  auto load_tiles = [&](int b) -> int {
+    return b < batch ? (cu_q[b + 1] - cu_q[b] + bm_tok - 1) / bm_tok : 0;
+  };
+  int nreg[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) nreg[c] = load_tiles(64 * c + lane);
+  auto tiles_of = [&](int c) -> int {  // this lane's sequence of chunk c
+    if (c < NC) {
+      int n = nreg[0];
+#pragma unroll
+      for (int cc = 1; cc < NC; ++cc)
+        if (c == cc) n = nreg[cc];
+      return n;
+    }
+    return load_tiles(64 * c + lane);
+  };
+  const int n_chunks = (batch + 63) / 64;
+  auto items_below = [&](int y) -> int64_t {  // P(y)
+    int part = 0;
+    for (int c = 0; c < n_chunks; ++c) part += min(tiles_of(c), y);
+    return static_cast<int64_t>(wave_sum_uniform(part)) * Hkv;
+  };
+  if (i >= items_below(max_tiles)) return false;
+  int lo = 0, hi = max_tiles;  // P(lo) <= i < P(hi)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (items_below(mid) <= i) lo = mid; else hi = mid;
+  }
+  const int64_t r = i - items_below(lo);
+  int k = static_cast<int>(r / Hkv);  // the k-th sequence with more than lo tiles
+  kvh_out = static_cast<int>(r - static_cast<int64_t>(k) * Hkv);
+  for (int c = 0; c < n_chunks; ++c) {
+    const int n = tiles_of(c);
+    const uint64_t mask = __ballot(n > lo);
+    const int cnt = __popcll(mask);
+    if (k < cnt) {
+      const int below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo(
+                                                      static_cast<uint32_t>(mask), 0u));
+      const uint64_t hit = __ballot(n > lo && below == k);
+      const int ln = __builtin_ctzll(hit);
+      b_out = 64 * c + ln;
+      tile_out = __builtin_amdgcn_readlane(n, ln) - 1 - lo;
+      return true;
+    }
+    k -= cnt;
+  }
+  return false;  // not reached for i inside the list
+}
+
 template <int D, int GP, bool BIG_BLOCK>
 __global__ __launch_bounds__(256, 2) void paged_prefill_bf16_kernel(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
     const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
     const int32_t* __restrict__ cu_seqlens_q, const int32_t* __restrict__ cu_seqlens_k,
     const int32_t* __restrict__ block_tables, int table_stride, int Hq, int Hkv, int G,
-    int bs_log2, float scale_log2) {
+    int bs_log2, float scale_log2, int batch, int max_tiles) {
   static_assert(D == 64 || D == 128, "head_dim");
   constexpr int BM_TOK = 128 / GP;  // tokens per workgroup tile
   constexpr int BN = 64;            // keys per K/V tile
@@ -72,14 +135,12 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_bf16_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][BN][KP];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][BN][KP];
 
-  const int b = blockIdx.x / Hkv;
-  const int kvh = blockIdx.x - b * Hkv;
+  int b = 0, kvh = 0, tile = 0;
+  if (!prefill_item(blockIdx.x, batch, Hkv, BM_TOK, max_tiles, cu_seqlens_q, b, kvh, tile))
+    return;  // past the item list: uniform over the workgroup, before any barrier
   const int q_begin = cu_seqlens_q[b];
   const int Lq = cu_seqlens_q[b + 1] - q_begin;
   const int Lk = cu_seqlens_k[b + 1] - cu_seqlens_k[b];
-  const int n_tiles = (Lq + BM_TOK - 1) / BM_TOK;
-  const int tile = n_tiles - 1 - static_cast<int>(blockIdx.y);
-  if (tile < 0) return;  // uniform, before any barrier
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -220,7 +281,11 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_bf16_kernel(
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sub][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
+    {  // lanes l and l^32 hold the two halves of a row: v_permlane32_swap pairs them
+      const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                       false, false);
+      mx = fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1])) * scale_log2;
+    }
     if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleSlack)) {  // wavefront-uniform
       const float m_new = fmaxf(m, mx);  // finite: key 0 of tile 0 is visible to every row
       const float alpha = __builtin_amdgcn_exp2f(m - m_new);
@@ -277,7 +342,11 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_bf16_kernel(
   }
 
   // ---- normalise and store: o[dt][r] is d = 32*dt + 8*(r/4) + 4*hi + r%4 of this row
-  l += __shfl_xor(l, 32, 64);
+  {
+    const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(l), __float_as_uint(l),
+                                                     false, false);
+    l = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+  }
   if (row_valid) {
     const float inv = 1.f / l;
     uint16_t* orow = out + (static_cast<int64_t>(q_begin + tok) * Hq + hq) * D;
@@ -297,14 +366,15 @@ template <int D, int GP>
 static void launch_prefill(dim3 grid, hipStream_t stream, const void* q, void* out,
                            const void* kc, const void* vc, const int32_t* cu_q,
                            const int32_t* cu_k, const int32_t* tables, int stride, int Hq,
-                           int Hkv, int G, int bs_log2, float scale_log2) {
+                           int Hkv, int G, int bs_log2, float scale_log2, int batch,
+                           int max_tiles) {
   // blocks of at least 64 tokens hold a whole 64-key tile
   auto kernel = bs_log2 >= 6 ? paged_prefill_bf16_kernel<D, GP, true>
                              : paged_prefill_bf16_kernel<D, GP, false>;
   hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<uint16_t*>(out),
                      static_cast<const uint16_t*>(kc), static_cast<const uint16_t*>(vc), cu_q,
-                     cu_k, tables, stride, Hq, Hkv, G, bs_log2, scale_log2);
+                     cu_k, tables, stride, Hq, Hkv, G, bs_log2, scale_log2, batch, max_tiles);
 }
 
 hipError_t launch_paged_prefill_bf16(int head_dim, const void* q, void* out, const void* k_cache,
@@ -318,15 +388,16 @@ hipError_t launch_paged_prefill_bf16(int head_dim, const void* q, void* out, con
   const int GP = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : G <= 8 ? 8 : G <= 16 ? 16 : G <= 32
                  ? 32 : G <= 64 ? 64 : 128;
   const int bm_tok = 128 / GP;
-  const int64_t xs = static_cast<int64_t>(batch) * num_kv_heads;
   const int max_tiles = (max_seqlen_q + bm_tok - 1) / bm_tok;
-  if (xs > 0x7fffffff || max_tiles > 65535) return hipErrorInvalidConfiguration;
-  const dim3 grid(static_cast<unsigned>(xs), max_tiles);
+  // one workgroup per (sequence, kv head, q tile) at most; the real items come first
+  const int64_t slots = static_cast<int64_t>(batch) * num_kv_heads * max_tiles;
+  if (slots > 0x7fffffff) return hipErrorInvalidConfiguration;
+  const dim3 grid(static_cast<unsigned>(slots));
   const float scale_log2 = scale * kLog2e;
 #define PKV_PF(D_, GP_)                                                                       \
   launch_prefill<D_, GP_>(grid, stream, q, out, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k, \
                           block_tables, table_stride, num_q_heads, num_kv_heads, G, bs_log2,  \
-                          scale_log2)
+                          scale_log2, batch, max_tiles)
 #define PKV_PF_GP(D_)                                  \
   switch (GP) {                                        \
     case 1: PKV_PF(D_, 1); break;                      \
