@@ -41,6 +41,7 @@
 #include <algorithm>
 #include <atomic>
 
+#include "decode_plan.h"
 #include "device.h"
 #include "launch.h"
 #include "timing.h"
@@ -105,17 +106,6 @@ __device__ __forceinline__ u32x4_t load_stream(const uint16_t* base, uint32_t by
       reinterpret_cast<const u32x4_t*>(reinterpret_cast<const char*>(base) + byte_off));
 }
 
-// chunks of a sequence of length L
-template <int CH>
-__device__ __forceinline__ int chunks_of(int L) {
-  return (max(L, 0) + CH - 1) / CH;
-}
-
-// worker owning chunk c of C when C chunks are split over W workers as [w*C/W, (w+1)*C/W)
-__device__ __forceinline__ int64_t worker_of(int64_t c, int64_t C, int64_t W) {
-  return ((c + 1) * W - 1) / C;
-}
-
 // Position of a worker in the chunk list; every field is wavefront-uniform.
 struct Cursor {
   int b;    // sequence
@@ -136,7 +126,7 @@ struct KVBuf {
 
 }  // namespace
 
-template <int D, int GP, int CH, bool ONE_BLOCK>
+template <int D, int GP, bool ONE_BLOCK>
 __global__ __launch_bounds__(256) void paged_decode_bf16_kernel(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
     const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
@@ -146,6 +136,7 @@ __global__ __launch_bounds__(256) void paged_decode_bf16_kernel(
     float2* __restrict__ ws_ml, float* __restrict__ ws_o) {
   static_assert(D == 64 || D == 128, "head_dim");
   static_assert(GP == 1 || GP == 2 || GP == 4 || GP == 8, "heads per stream");
+  constexpr int CH = kDecodeChunk;
   static_assert(CH == 16 || CH == 32, "chunk");
   constexpr int KK = D / 32;           // MFMA k-steps over head_dim
   constexpr int DCH = D / 8;           // 16-byte pieces per row
@@ -175,7 +166,7 @@ __global__ __launch_bounds__(256) void paged_decode_bf16_kernel(
   // also records every sequence's first chunk for the combine kernel.
   int64_t tot = 0;
   for (int b0 = 0; b0 < batch; b0 += 64)
-    if (b0 + lane < batch) tot += static_cast<int64_t>(chunks_of<CH>(context_lens[b0 + lane])) * S;
+    if (b0 + lane < batch) tot += static_cast<int64_t>(chunks_of(context_lens[b0 + lane])) * S;
   const int64_t C = read_lane64(wave_sum64(tot), 0);
   const int64_t W = num_workers;
   const int64_t c_begin = worker * C / W;
@@ -186,7 +177,7 @@ __global__ __launch_bounds__(256) void paged_decode_bf16_kernel(
     int64_t carry = 0;
     for (int b0 = 0; b0 < batch; b0 += 64) {
       const int b = b0 + lane;
-      const int64_t n = b < batch ? static_cast<int64_t>(chunks_of<CH>(context_lens[b])) * S : 0;
+      const int64_t n = b < batch ? static_cast<int64_t>(chunks_of(context_lens[b])) * S : 0;
       int64_t incl = n;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
@@ -213,7 +204,7 @@ __global__ __launch_bounds__(256) void paged_decode_bf16_kernel(
   Cursor cur;
   cur.b = b_first;
   cur.L = context_lens[b_first];
-  cur.nch = chunks_of<CH>(cur.L);
+  cur.nch = chunks_of(cur.L);
   {
     const int64_t r = c_begin - p_first;
     cur.j = static_cast<int>(r / cur.nch);
@@ -227,7 +218,7 @@ __global__ __launch_bounds__(256) void paged_decode_bf16_kernel(
         do {  // the list holds a later chunk, so a sequence with chunks follows
           ++x.b;
           x.L = context_lens[x.b];
-          x.nch = chunks_of<CH>(x.L);
+          x.nch = chunks_of(x.L);
         } while (x.nch == 0);
       }
     }
@@ -524,61 +515,9 @@ __global__ __launch_bounds__(256) void paged_decode_bf16_kernel(
   }
 }
 
-// Merge of the per-worker partials of every stream that was cut between workers.
-// Grid: (stream within sequence, sequence).
-template <int D, int GP, int CH>
-__global__ __launch_bounds__(128) void decode_combine_kernel(
-    const int64_t* __restrict__ ws_prefix, const float2* __restrict__ ws_ml,
-    const float* __restrict__ ws_o, uint16_t* __restrict__ out,
-    const int32_t* __restrict__ context_lens, int batch, int Hq, int G, int n_hg,
-    int num_workers) {
-  const int j = blockIdx.x;
-  const int b = blockIdx.y;
-  const int nch = chunks_of<CH>(context_lens[b]);
-  if (nch == 0) return;
-  const int64_t C = ws_prefix[batch];
-  const int64_t W = num_workers;
-  const int64_t cs = ws_prefix[b] + static_cast<int64_t>(j) * nch;
-  const int64_t ce = cs + nch - 1;
-  const int64_t wa = worker_of(cs, C, W);
-  const int64_t wb = worker_of(ce, C, W);
-  if (wa == wb) return;  // finished by one worker
-  const int kvh = j / n_hg;
-  const int hg = j - kvh * n_hg;
-  const int nh = min(GP, G - hg * GP);
-  const int64_t hq0 = static_cast<int64_t>(b) * Hq + kvh * G + hg * GP;
-  const bool wa_second = wa * C / W < cs;  // worker wa had an earlier segment
-  for (int idx = threadIdx.x; idx < nh * D; idx += blockDim.x) {
-    const int h = idx / D;
-    const int d = idx - h * D;
-    float M = -INFINITY;
-    for (int64_t w = wa; w <= wb; ++w) {
-      if (w > wa && w * C / W == (w + 1) * C / W) continue;  // empty range
-      const int64_t slot = 2 * w + (w == wa && wa_second ? 1 : 0);
-      M = fmaxf(M, ws_ml[slot * GP + h].x);
-    }
-    float lsum = 0.f, osum = 0.f;
-    for (int64_t w = wa; w <= wb; ++w) {
-      if (w > wa && w * C / W == (w + 1) * C / W) continue;
-      const int64_t slot = 2 * w + (w == wa && wa_second ? 1 : 0);
-      const float2 ml = ws_ml[slot * GP + h];
-      const float f = exp2f(ml.x - M);
-      lsum += f * ml.y;
-      osum += f * ws_o[(slot * GP + h) * D + d];
-    }
-    out[(hq0 + h) * D + d] = static_cast<uint16_t>(f32_to_bf16_bits(osum / lsum));
-  }
-}
-
 namespace {
 
-int heads_per_stream(int G) { return G >= 8 ? 8 : (G >= 4 ? 4 : (G >= 2 ? 2 : 1)); }
-
-constexpr int kMaxAutoWorkers = 4096;
-
-size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
-
-template <int D, int GP, int CH, bool ONE_BLOCK>
+template <int D, int GP, bool ONE_BLOCK>
 int auto_workers() {
   static std::atomic<int> cached[64];
   int dev = 0;
@@ -588,7 +527,7 @@ int auto_workers() {
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu, reinterpret_cast<const void*>(&paged_decode_bf16_kernel<D, GP, CH, ONE_BLOCK>), 256, 0) !=
+          &per_cu, reinterpret_cast<const void*>(&paged_decode_bf16_kernel<D, GP, ONE_BLOCK>), 256, 0) !=
           hipSuccess ||
       cus <= 0 || per_cu <= 0) {
     cus = 256;
@@ -599,7 +538,7 @@ int auto_workers() {
   return w;
 }
 
-template <int D, int GP, int CH, bool ONE_BLOCK>
+template <int D, int GP, bool ONE_BLOCK>
 hipError_t launch_decode(const void* q, void* out, const void* k_cache, const void* v_cache,
                          int num_q_heads, int num_kv_heads, int bs_log2, int batch,
                          const int32_t* context_lens, const int32_t* block_tables,
@@ -609,27 +548,20 @@ hipError_t launch_decode(const void* q, void* out, const void* k_cache, const vo
   const int n_hg = (G + GP - 1) / GP;
   const int S = num_kv_heads * n_hg;
   if (S > 65535) return hipErrorInvalidConfiguration;
-  const int W = num_workers > 0 ? num_workers : auto_workers<D, GP, CH, ONE_BLOCK>();
-  int64_t* ws_prefix = static_cast<int64_t*>(workspace);
-  char* base = static_cast<char*>(workspace) + align256(sizeof(int64_t) * (batch + 1));
-  float2* ws_ml = reinterpret_cast<float2*>(base);
-  float* ws_o = reinterpret_cast<float*>(base + align256(sizeof(float2) * 2 * W * GP));
+  const int W = num_workers > 0 ? num_workers : auto_workers<D, GP, ONE_BLOCK>();
+  const DecodeWorkspace ws = carve_decode_workspace(workspace, batch, W, GP);
   const float scale_log2 = scale * kLog2e;
   timing_begin("paged_decode", stream);
-  hipLaunchKernelGGL((paged_decode_bf16_kernel<D, GP, CH, ONE_BLOCK>), dim3((W + 3) / 4), dim3(256), 0,
+  hipLaunchKernelGGL((paged_decode_bf16_kernel<D, GP, ONE_BLOCK>), dim3((W + 3) / 4), dim3(256), 0,
                      stream, static_cast<const uint16_t*>(q), static_cast<uint16_t*>(out),
                      static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache),
                      context_lens, block_tables, table_stride, batch, num_q_heads, num_kv_heads,
-                     G, n_hg, bs_log2, scale_log2, W, ws_prefix, ws_ml, ws_o);
+                     G, n_hg, bs_log2, scale_log2, W, ws.prefix, ws.ml, ws.o);
   timing_end(stream);
-  hipError_t e = hipGetLastError();
+  const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  timing_begin("paged_decode_combine", stream);
-  hipLaunchKernelGGL((decode_combine_kernel<D, GP, CH>), dim3(S, batch), dim3(128), 0, stream,
-                     ws_prefix, ws_ml, ws_o, static_cast<uint16_t*>(out), context_lens, batch,
-                     num_q_heads, G, n_hg, W);
-  timing_end(stream);
-  return hipGetLastError();
+  return launch_decode_combine(D, GP, ws, out, context_lens, batch, num_q_heads, num_kv_heads, W,
+                               stream);
 }
 
 }  // namespace
@@ -637,9 +569,8 @@ hipError_t launch_decode(const void* q, void* out, const void* k_cache, const vo
 size_t paged_decode_bf16_workspace(int head_dim, int num_q_heads, int num_kv_heads, int batch,
                                    int num_workers) {
   const int GP = heads_per_stream(num_q_heads / num_kv_heads);
-  const size_t W = num_workers > 0 ? static_cast<size_t>(num_workers) : kMaxAutoWorkers;
-  return align256(sizeof(int64_t) * (static_cast<size_t>(batch) + 1)) +
-         align256(sizeof(float2) * 2 * W * GP) + sizeof(float) * 2 * W * GP * head_dim;
+  return decode_workspace_bytes(batch, num_workers > 0 ? num_workers : kMaxAutoWorkers, GP,
+                                head_dim);
 }
 
 hipError_t launch_paged_decode_bf16(int head_dim, const void* q, void* out, const void* k_cache,
@@ -647,32 +578,31 @@ hipError_t launch_paged_decode_bf16(int head_dim, const void* q, void* out, cons
                                     int bs_log2, int batch, const int32_t* context_lens,
                                     const int32_t* block_tables, int table_stride, float scale,
                                     int num_workers, void* workspace, hipStream_t stream) {
-  // 16-token chunks: two of them in flight per wave keep enough bytes outstanding
-  // while leaving registers for several waves per SIMD
+  // ONE_BLOCK: every 16-token chunk lies in one block (block_size >= 16)
   const int GP = heads_per_stream(num_q_heads / num_kv_heads);
-#define PKV_DEC(D_, GP_, CH_)                                                                \
-  return bs_log2 >= 4                                                                        \
-             ? launch_decode<D_, GP_, CH_, true>(q, out, k_cache, v_cache, num_q_heads,     \
-                                                 num_kv_heads, bs_log2, batch, context_lens, \
-                                                 block_tables, table_stride, scale,          \
-                                                 num_workers, workspace, stream)             \
-             : launch_decode<D_, GP_, CH_, false>(q, out, k_cache, v_cache, num_q_heads,    \
-                                                  num_kv_heads, bs_log2, batch, context_lens, \
-                                                  block_tables, table_stride, scale,         \
-                                                  num_workers, workspace, stream)
+#define PKV_DEC(D_, GP_)                                                                    \
+  return bs_log2 >= 4                                                                       \
+             ? launch_decode<D_, GP_, true>(q, out, k_cache, v_cache, num_q_heads,          \
+                                            num_kv_heads, bs_log2, batch, context_lens,      \
+                                            block_tables, table_stride, scale, num_workers,  \
+                                            workspace, stream)                               \
+             : launch_decode<D_, GP_, false>(q, out, k_cache, v_cache, num_q_heads,         \
+                                             num_kv_heads, bs_log2, batch, context_lens,     \
+                                             block_tables, table_stride, scale, num_workers, \
+                                             workspace, stream)
   if (head_dim == 128) {
     switch (GP) {
-      case 1: PKV_DEC(128, 1, 16);
-      case 2: PKV_DEC(128, 2, 16);
-      case 4: PKV_DEC(128, 4, 16);
-      default: PKV_DEC(128, 8, 16);
+      case 1: PKV_DEC(128, 1);
+      case 2: PKV_DEC(128, 2);
+      case 4: PKV_DEC(128, 4);
+      default: PKV_DEC(128, 8);
     }
   }
   switch (GP) {
-    case 1: PKV_DEC(64, 1, 16);
-    case 2: PKV_DEC(64, 2, 16);
-    case 4: PKV_DEC(64, 4, 16);
-    default: PKV_DEC(64, 8, 16);
+    case 1: PKV_DEC(64, 1);
+    case 2: PKV_DEC(64, 2);
+    case 4: PKV_DEC(64, 4);
+    default: PKV_DEC(64, 8);
   }
 #undef PKV_DEC
 }
