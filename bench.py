@@ -14,9 +14,10 @@ are bracketed by a device synchronisation on both sides.
 
 Printed: ONE JSON line.  ``value`` is the step's algorithmic HBM bytes (K and V
 of every context token, q, out, the new tokens' K/V read and written, and the
-metadata used) divided by the step time.  ``roofline`` is for the dominant
-kernel (decode), its duration measured with HIP events on its own stream
-inside the timed region.  ``prefill`` reports the varlen causal prefill (16 q /
+metadata used) divided by the step time, timed without per-kernel events.
+``roofline`` is for the dominant kernel (decode): its duration is measured with
+HIP events recorded on its own stream around each launch, in a second timed pass
+over the same K steps.  ``prefill`` reports the varlen causal prefill (16 q /
 8 kv heads, 16 prompts of length uniform on [128, 2048]) in TFLOP/s over the
 unmasked causal pairs.  ``cpu_baseline`` times the CPU oracle on a bounded
 sample of the same decode workload, on this host's cores.
@@ -112,10 +113,11 @@ def measured_traffic():
         return None
 
 
-def timed_steps(torch, pkv, fn, steps):
-    """Run fn `steps` times between two synchronisations with kernel timing on."""
+def timed_steps(torch, pkv, fn, steps, kernel_events: bool):
+    """Run fn `steps` times between two device synchronisations; with kernel_events the
+    library brackets each of its launches with HIP events on the launch's stream."""
     pkv.timing_collect()
-    pkv.timing_enable(True)
+    pkv.timing_enable(kernel_events)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -183,7 +185,7 @@ def prefill_leg(torch, pkv, workloads, DeviceStep, args) -> dict:
     for _ in range(3):
         ps.run()
     torch.cuda.synchronize()
-    _, _, pk = timed_steps(torch, pkv, ps.prefill, max(5, args.steps // 5))
+    _, _, pk = timed_steps(torch, pkv, ps.prefill, max(5, args.steps // 5), kernel_events=True)
     pname = max((k for k in pk if "prefill" in k), key=lambda k: pk[k]["total_ms"])
     flops = prefill_flops(wp, ps.plan)
     tflops = flops / (pk[pname]["avg_ms"] * 1e-3) / 1e12
@@ -247,8 +249,12 @@ def main():
     for _ in range(args.warmup):
         step.run()
     torch.cuda.synchronize()
-    ms_total, wall, kernels = timed_steps(torch, pkv, step.run, args.steps)
+    # The step time comes from a pass without per-kernel events (each event pair adds
+    # about 10 us of command-processor time before its launch); the kernel durations
+    # of the roofline come from a second timed pass over the same steps with them.
+    ms_total, wall, _ = timed_steps(torch, pkv, step.run, args.steps, kernel_events=False)
     ms_per_step = ms_total / args.steps
+    _, _, kernels = timed_steps(torch, pkv, step.run, args.steps, kernel_events=True)
     d_bytes = decode_bytes(wl, plan)
     s_bytes = store_bytes(wl, n_new)
     value = (d_bytes + s_bytes) / (ms_per_step * 1e-3) / 1e9

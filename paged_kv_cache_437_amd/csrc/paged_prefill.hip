@@ -20,8 +20,9 @@
 //                                row-major V tile, B = P converted to bf16 in place.
 // The key order inside each MFMA k-step is the same permutation for both operands,
 // so the P registers produced by the S^T MFMA feed the O^T MFMA without shuffles.
-// K/V tiles are double buffered in LDS with rows padded to (D + 16) elements (no
-// bank conflicts for the 16-byte and the transposing reads); tile j+1 is fetched
+// K/V tiles are double buffered in LDS with rows padded to D + 8 (K) and D + 32 (V)
+// elements, the pitches with the fewest bank conflicts for the 16-byte and the
+// transposing reads; tile j+1 is fetched
 // into registers while tile j is computed.  Keys at or past Lk re-read the tile's
 // last valid key (stale rows never enter; their scores are masked), table entries
 // past the last used block are never read, and causal masking is applied only on
@@ -121,7 +122,12 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_bf16_kernel(
   static_assert(D == 64 || D == 128, "head_dim");
   constexpr int BM_TOK = 128 / GP;  // tokens per workgroup tile
   constexpr int BN = 64;            // keys per K/V tile
-  constexpr int KP = D + 16;        // padded LDS row (elements)
+  // LDS row pitches (elements).  K is read 16 bytes per lane, one row per lane: a pitch
+  // of D + 8 puts 16 consecutive rows on distinct banks.  V is read 8 bytes per lane by
+  // the transposing reads, 4 rows x 64 bytes per half-wave: a pitch of D + 32 spreads
+  // those rows (both measured fastest among D + 0/8/16/32 on gfx950).
+  constexpr int KPK = D + 8;
+  constexpr int KPV = D + 32;
   constexpr int KS = D / 16;        // S^T MFMA k-steps over head_dim
   constexpr int DT = D / 32;        // O^T tiles of 32 head_dim rows
   constexpr int CPR = D / 8;        // 16-byte chunks per K/V row
@@ -132,8 +138,8 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_bf16_kernel(
   // skip the rescale of the accumulators; probabilities stay <= 2^8.
   constexpr float kRescaleSlack = 8.f;
 
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][BN][KP];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][BN][KP];
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][BN][KPK];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][BN][KPV];
 
   int b = 0, kvh = 0, tile = 0;
   if (!prefill_item(blockIdx.x, batch, Hkv, BM_TOK, max_tiles, cu_seqlens_q, b, kvh, tile))
@@ -328,7 +334,7 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_bf16_kernel(
       for (int dt = 0; dt < DT; ++dt) {
         const uint16_t* p0 = &v_lds[buf][16 * ks + key_in][32 * dt + col_in];
         const i16x4_t lo4 = lds_read_tr16(p0);
-        const i16x4_t hi4 = lds_read_tr16(p0 + 8 * KP);
+        const i16x4_t hi4 = lds_read_tr16(p0 + 8 * KPV);
         const u32x2_t lo = __builtin_bit_cast(u32x2_t, lo4);
         const u32x2_t hi2 = __builtin_bit_cast(u32x2_t, hi4);
         const u32x4_t va = {lo[0], lo[1], hi2[0], hi2[1]};
