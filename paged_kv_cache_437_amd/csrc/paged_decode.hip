@@ -20,17 +20,21 @@
 // once, and streaming them past the caches is what lets the read approach the HBM
 // peak.  The cut depends only on lengths and W, never on block ids.
 //
-// Per chunk and worker:
-//   * K rows go straight from HBM into the B operand of v_mfma_f32_16x16x32_bf16
-//     (lane: token lane%16, 8 head_dim elements), the A operand holding the group's
-//     q rows (padded to 16), so every grouped q head reuses each K row loaded;
+// Per chunk and worker, K and V are read alike: lane (sub, piece) loads 16 bytes,
+// piece `piece` of one row, so each load instruction covers whole rows (whole
+// 128-byte lines, the access pattern HBM streams fastest).  Then, on the vector ALU:
+//   * scores: per head, the q piece . K piece (bf16 pair dot products, fp32
+//     accumulation), summed over the row's lanes with DPP moves; every grouped q head
+//     reuses each K row loaded;
 //   * online softmax in the log2 domain (scale * log2 e folded into one multiply):
-//     row max across the 16 lanes of a tile row, exp2, per-lane partial sums;
-//   * probabilities go through a per-wave LDS tile to the P.V phase, where lanes
-//     own (token, 8 head_dim elements) of V rows loaded with 16-byte loads and
-//     accumulate on the vector ALU.
-// All K/V loads are predicated on token < context_len, so neither table entries past
-// the last used block nor the stale tail of the last block is ever read.
+//     max over the chunk's rows with DPP and v_permlane16/32_swap, exp2, per-lane
+//     shares of the row sum;
+//   * P.V: each lane accumulates its rows' weighted V pieces; the lanes holding one
+//     head_dim piece are summed once, at the end of the segment.
+// Rows past context_len are never read: the buffer loads' range check returns zeros
+// for them (block_size >= 16), or they re-read the chunk's last valid row (smaller
+// blocks), so neither the stale tail of the last block nor a table entry past it is
+// ever touched; their scores are masked to -inf.
 //
 // A stream whose chunks all fall to one worker is finished by it and written as
 // bf16.  A stream cut between workers leaves one fp32 partial (max, sum,
@@ -52,26 +56,10 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 namespace {
 
-// Reductions over the 16 lanes of a row with DPP lane moves (quad swaps, then the
-// half-row and row mirrors): every lane of the row ends with the result.
+// DPP lane move within rows of 16 lanes (all rows and banks enabled)
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float row16_max(float x) {
-  x = fmaxf(x, dpp<0xB1>(x));   // quad_perm [1,0,3,2]
-  x = fmaxf(x, dpp<0x4E>(x));   // quad_perm [2,3,0,1]
-  x = fmaxf(x, dpp<0x141>(x));  // row_half_mirror
-  return fmaxf(x, dpp<0x140>(x));  // row_mirror
-}
-__device__ __forceinline__ float row16_sum(float x) {
-  x += dpp<0xB1>(x);
-  x += dpp<0x4E>(x);
-  x += dpp<0x141>(x);
-  return x + dpp<0x140>(x);
-}
-__device__ __forceinline__ float read_lane(float x, int lane) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
 }
 __device__ __forceinline__ int64_t read_lane64(int64_t x, int lane) {
   const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(x), lane);
@@ -95,17 +83,15 @@ __device__ __forceinline__ int64_t wave_sum64(int64_t x) {
   return x;
 }
 
+// Buffer descriptor word 3 for gfx9-family raw buffers (32-bit data format, no
+// swizzle), and the cache-policy bit of a non-temporal buffer load.
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kNonTemporal = 2;
+
 // K/V rows are read once: non-temporal loads stream them past the caches.
 __device__ __forceinline__ u32x4_t load_stream(const uint16_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
 }
-// Wavefront-uniform base plus a 32-bit per-lane byte offset: one address register
-// per lane and the scalar-base form of the load.
-__device__ __forceinline__ u32x4_t load_stream(const uint16_t* base, uint32_t byte_off) {
-  return __builtin_nontemporal_load(
-      reinterpret_cast<const u32x4_t*>(reinterpret_cast<const char*>(base) + byte_off));
-}
-
 // Position of a worker in the chunk list; every field is wavefront-uniform.
 struct Cursor {
   int b;    // sequence
@@ -115,14 +101,66 @@ struct Cursor {
   int k;    // chunk within the stream
 };
 
-// One chunk's operands in registers: K rows as MFMA B operands, V rows as 16-byte
-// (token, 8 head_dim elements) pieces, and the stream's q rows as the A operand.
-template <int D, int CH>
+// One chunk's operands in registers, K and V alike: lane (token, 16-byte piece) as
+// in a whole-row load (every load instruction covers whole rows: whole 128-byte
+// lines, the pattern HBM streams fastest), plus this lane's piece of each q row of
+// the stream.
+template <int D, int CH, int GP>
 struct KVBuf {
-  u32x4_t k[CH / 16][D / 32];
-  u32x4_t v[CH * (D / 8) / 64];
-  u32x4_t q[D / 32];
+  static constexpr int N = CH * (D / 8) / 64;  // 16-byte pieces per lane (K and V each)
+  u32x4_t k[N];
+  u32x4_t v[N];
+  u32x4_t q[GP];
 };
+
+// q . k over one 16-byte piece (8 products as 4 bf16 pair dot products, fp32
+// accumulation)
+__device__ __forceinline__ float dot_piece(u32x4_t a, u32x4_t b) {
+  const bf16x8_t x = __builtin_bit_cast(bf16x8_t, a);
+  const bf16x8_t y = __builtin_bit_cast(bf16x8_t, b);
+  float c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 0, 1),
+                                            __builtin_shufflevector(y, y, 0, 1), 0.f, false);
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 2, 3),
+                                      __builtin_shufflevector(y, y, 2, 3), c, false);
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 4, 5),
+                                      __builtin_shufflevector(y, y, 4, 5), c, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 6, 7),
+                                         __builtin_shufflevector(y, y, 6, 7), c, false);
+}
+
+// Sum over the DCH lanes that hold one token's pieces (16 lanes = a DPP row at head_dim
+// 128, 8 lanes = half a row at 64); every one of them gets the sum.
+template <int DCH>
+__device__ __forceinline__ float piece_sum(float x) {
+  x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp<0x141>(x);  // row_half_mirror
+  if constexpr (DCH == 16) x += dpp<0x140>(x);  // row_mirror
+  return x;
+}
+
+// Max / sum over the token groups of a wavefront (lanes l, l^8 (half rows, head_dim 64
+// only), l^16, l^32): DPP row_ror:8 and v_permlane16/32_swap, no LDS.
+template <int DCH>
+__device__ __forceinline__ float token_max(float x) {
+  if constexpr (DCH == 8) x = fmaxf(x, dpp<0x128>(x));  // row_ror:8
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+template <int DCH>
+__device__ __forceinline__ float token_sum(float x) {
+  if constexpr (DCH == 8) x += dpp<0x128>(x);  // row_ror:8
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
 
 }  // namespace
 
@@ -138,15 +176,10 @@ __global__ __launch_bounds__(256) void paged_decode_bf16_kernel(
   static_assert(GP == 1 || GP == 2 || GP == 4 || GP == 8, "heads per stream");
   constexpr int CH = kDecodeChunk;
   static_assert(CH == 16 || CH == 32, "chunk");
-  constexpr int KK = D / 32;           // MFMA k-steps over head_dim
-  constexpr int DCH = D / 8;           // 16-byte pieces per row
-  constexpr int TPI = 64 / DCH;        // tokens per V load instruction
-  constexpr int VIT = CH / TPI;        // V loads per lane per chunk
-  constexpr int T16 = CH / 16;         // 16-token score tiles per chunk
-  constexpr int RR = GP < 4 ? GP : 4;  // head rows a lane keeps softmax state for
-  typedef KVBuf<D, CH> Buf;
-
-  __shared__ __attribute__((aligned(16))) float p_lds[4][CH][16];
+  constexpr int DCH = D / 8;     // 16-byte pieces per row
+  constexpr int TPI = 64 / DCH;  // rows per load instruction
+  constexpr int VIT = CH / TPI;  // K (and V) loads per lane per chunk
+  typedef KVBuf<D, CH, GP> Buf;
 
   // wave index through readfirstlane: the compiler then knows everything derived
   // from it (the worker's chunk range and cursor) is wavefront-uniform
@@ -154,10 +187,8 @@ __global__ __launch_bounds__(256) void paged_decode_bf16_kernel(
   const int lane = threadIdx.x & 63;
   const int worker = blockIdx.x * 4 + wave;
   if (worker >= num_workers) return;  // wavefront-uniform; the kernel has no block barrier
-  const int row = lane & 15;  // MFMA: token column (B) / head row (A)
-  const int grp = lane >> 4;  // MFMA: 8-element slice of each 32-wide k-step
-  const int v_chunk = lane % DCH;
-  const int v_sub = lane / DCH;
+  const int piece = lane % DCH;  // 16-byte piece of a row: head_dim [8*piece, 8*piece+8)
+  const int sub = lane / DCH;    // row within a load instruction
   const int S = Hkv * n_hg;
   const int bs_mask = (1 << bs_log2) - 1;
   const uint32_t row_bytes = static_cast<uint32_t>(Hkv) * D * 2;  // token stride in a block
@@ -223,158 +254,123 @@ __global__ __launch_bounds__(256) void paged_decode_bf16_kernel(
       }
     }
   };
-  // Block id of this lane's token of the chunk (a vector load, so its wait counts in
-  // order with the K/V loads); with ONE_BLOCK every lane gets the same id.
+  // Block id of the chunk's rows.  With ONE_BLOCK the chunk lies in one block, so the
+  // address is wavefront-uniform (a scalar load); otherwise lane t < CH gets the block
+  // of row t (clamped to the context: table entries past the last used block are
+  // never read).
   auto table_entry = [&](const Cursor& x) -> int {
+    if constexpr (ONE_BLOCK)
+      return block_tables[static_cast<int64_t>(x.b) * table_stride + ((x.k * CH) >> bs_log2)];
     const int tok = min(x.k * CH + (lane & (CH - 1)), x.L - 1);
     return block_tables[static_cast<int64_t>(x.b) * table_stride + (tok >> bs_log2)];
   };
-  // Every load of a chunk is issued without a condition, so the compiler's waits
-  // count them in order: rows past the context re-read the chunk's last valid row
-  // (real data, never stale memory; their scores are masked and their V rows get
-  // weight 0), q rows past the stream's heads re-read its first row (zeroed when
-  // used), and a `live` == false chunk (the one after a worker's last) reads one row.
+  // Lane (sub, piece) reads piece `piece` of rows it*TPI + sub.  Every load of a chunk
+  // is issued without a condition, so the compiler's waits count them in order.
+  // With ONE_BLOCK the chunk lies in one block and K, V and q are read with buffer
+  // loads: a wavefront-uniform descriptor (base = the chunk's first row) plus the
+  // loop-invariant 32-bit lane offsets `kv_off`, so issuing writes no vector register
+  // but the load destinations (a vector temporary there would make the compiler wait
+  // for loads still in flight).  The descriptor's size ends at the context: rows past
+  // it (the stale tail of the last block) come back as zeros without a memory access,
+  // and so do q rows past the stream's heads.  Without ONE_BLOCK a chunk spans several
+  // blocks: rows past the context re-read the chunk's last valid row (their weight is
+  // exactly 0) and q rows past the stream's heads re-read its first row (those heads
+  // are never written out).  A `live` == false chunk (the one after a worker's last)
+  // repeats the worker's last chunk.
+  uint32_t kv_off[VIT];
+#pragma unroll
+  for (int it = 0; it < VIT; ++it)
+    kv_off[it] = static_cast<uint32_t>(it * TPI + sub) * row_bytes + piece * 16;
   auto issue = [&](const Cursor& x, int te, Buf& buf, bool live) {
     const int kvh = n_hg == 1 ? x.j : x.j / n_hg;
     const int hg = x.j - kvh * n_hg;
     const int tok0 = x.k * CH;
-    const int last = live ? min(x.L - tok0, CH) - 1 : 0;  // last row read
-    {
-      const uint16_t* qb = q + (static_cast<int64_t>(x.b) * Hq + kvh * G + hg * GP) * D;
-      const int qrow = (live && row < min(GP, G - hg * GP)) ? row : 0;
-      const uint32_t off = static_cast<uint32_t>(qrow * D + grp * 8) * 2;
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
-        buf.q[kk] = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const char*>(qb) + off +
-                                                      kk * 64);
-    }
+    const int nh = min(GP, G - hg * GP);
+    const uint16_t* qb = q + (static_cast<int64_t>(x.b) * Hq + kvh * G + hg * GP) * D;
     if constexpr (ONE_BLOCK) {
-      // block_size >= CH: the chunk lies in one block, so a uniform base and 32-bit
-      // lane offsets address it
+      (void)live;
+      const auto qr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(qb), 0, nh * D * 2,
+                                                        kBufferWord3);
+#pragma unroll
+      for (int h = 0; h < GP; ++h)
+        buf.q[h] = __builtin_amdgcn_raw_buffer_load_b128(qr, piece * 16 + h * D * 2, 0, 0);
       const int64_t blk = __builtin_amdgcn_readfirstlane(te);
       const int64_t first = ((blk << bs_log2) | (tok0 & bs_mask)) * Hkv + kvh;
-      const uint16_t* kb = k_cache + first * D;
-      const uint16_t* vb = v_cache + first * D;
-#pragma unroll
-      for (int t4 = 0; t4 < T16; ++t4) {
-        const uint32_t off = static_cast<uint32_t>(min(16 * t4 + row, last)) * row_bytes + grp * 16;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) buf.k[t4][kk] = load_stream(kb, off + kk * 64);
-      }
-#pragma unroll
-      for (int it = 0; it < VIT; ++it)
-        buf.v[it] = load_stream(
-            vb, static_cast<uint32_t>(min(it * TPI + v_sub, last)) * row_bytes + v_chunk * 16);
-    } else {
-      // small blocks: lane t holds the block of token tok0 + t
-#pragma unroll
-      for (int t4 = 0; t4 < T16; ++t4) {
-        const int tl = min(16 * t4 + row, last);
-        const int64_t off =
-            token_row(__shfl(te, tl, 64), tok0 + tl, bs_log2, Hkv, kvh, D) + grp * 8;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) buf.k[t4][kk] = load_stream(k_cache + off + kk * 32);
-      }
+      const int bytes = min(x.L - tok0, CH) * static_cast<int>(row_bytes);
+      const auto kr = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(k_cache + first * D), 0, bytes, kBufferWord3);
+      const auto vr = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(v_cache + first * D), 0, bytes, kBufferWord3);
 #pragma unroll
       for (int it = 0; it < VIT; ++it) {
-        const int tl = min(it * TPI + v_sub, last);
-        buf.v[it] = load_stream(
-            v_cache + token_row(__shfl(te, tl, 64), tok0 + tl, bs_log2, Hkv, kvh, D) +
-            v_chunk * 8);
+        buf.k[it] = __builtin_amdgcn_raw_buffer_load_b128(kr, kv_off[it], 0, kNonTemporal);
+        buf.v[it] = __builtin_amdgcn_raw_buffer_load_b128(vr, kv_off[it], 0, kNonTemporal);
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < GP; ++h)
+        buf.q[h] = *reinterpret_cast<const u32x4_t*>(qb + (h < nh ? h : 0) * D + piece * 8);
+      const int last = live ? min(x.L - tok0, CH) - 1 : 0;  // last row read
+#pragma unroll
+      for (int it = 0; it < VIT; ++it) {
+        const int tl = min(it * TPI + sub, last);
+        const int64_t off =
+            token_row(__shfl(te, tl, 64), tok0 + tl, bs_log2, Hkv, kvh, D) + piece * 8;
+        buf.k[it] = load_stream(k_cache + off);
+        buf.v[it] = load_stream(v_cache + off);
       }
     }
   };
 
-  // running softmax state of the current segment: rows r = head 4*grp + r
-  float m_r[RR], l_r[RR];
-  float o[GP][8];
+  // Running softmax state of the current segment, per head: the max m (log2 domain,
+  // the same in every lane), this lane's share of the sum (its rows' weights; the
+  // lanes of one row hold equal shares) and of the unnormalised output (its rows,
+  // head_dim [8*piece, 8*piece+8)).
+  float m[GP], l[GP], o[GP][8];
   auto reset = [&]() {
 #pragma unroll
-    for (int r = 0; r < RR; ++r) {
-      m_r[r] = -INFINITY;
-      l_r[r] = 0.f;
-    }
-#pragma unroll
-    for (int h = 0; h < GP; ++h)
+    for (int h = 0; h < GP; ++h) {
+      m[h] = -INFINITY;
+      l[h] = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
+    }
   };
   reset();
   bool first_segment = true;  // the worker's first segment takes partial slot 2w
   int seg_k0 = cur.k;         // chunk at which the current segment started
 
-  // one chunk into the running state (no memory writes besides the wave's LDS tile)
+  // one chunk into the running state (registers only: no memory access)
   auto accumulate = [&](const Cursor& x, const Buf& buf) {
-    const int valid = x.L - x.k * CH;  // tokens of the chunk inside the context
-    const int kvh = n_hg == 1 ? x.j : x.j / n_hg;
-    const int hg = x.j - kvh * n_hg;
-    const int nh = min(GP, G - hg * GP);
-    // ---- scores: S[head 4*grp + r][token 16*t4 + row] in acc[t4][r]
-    const u32x4_t zero = {0u, 0u, 0u, 0u};
-    f32x4_t acc[T16];
-#pragma unroll
-    for (int t4 = 0; t4 < T16; ++t4) {
-      acc[t4] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
-        acc[t4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8_t, row < nh ? buf.q[kk] : zero),
-            __builtin_bit_cast(bf16x8_t, buf.k[t4][kk]), acc[t4], 0, 0, 0);
-    }
-    // ---- online softmax (log2 domain), per head row
-    float alpha_r[RR];
-#pragma unroll
-    for (int r = 0; r < RR; ++r) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int t4 = 0; t4 < T16; ++t4) {
-        const float s = (16 * t4 + row < valid) ? acc[t4][r] * scale_log2 : -INFINITY;
-        acc[t4][r] = s;
-        mx = fmaxf(mx, s);
-      }
-      const float m_new = fmaxf(m_r[r], row16_max(mx));  // finite: the chunk's row 0 is valid
-      alpha_r[r] = __builtin_amdgcn_exp2f(m_r[r] - m_new);
-      float sum = 0.f;
-#pragma unroll
-      for (int t4 = 0; t4 < T16; ++t4) {
-        const float p = __builtin_amdgcn_exp2f(acc[t4][r] - m_new);
-        acc[t4][r] = p;
-        sum += p;
-      }
-      l_r[r] = l_r[r] * alpha_r[r] + sum;
-      m_r[r] = m_new;
-    }
-#pragma unroll
-    for (int t4 = 0; t4 < T16; ++t4)
-      *reinterpret_cast<f32x4_t*>(&p_lds[wave][16 * t4 + row][4 * grp]) = acc[t4];
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    // ---- rescale and accumulate P.V on the vector ALU
+    const int valid = x.L - x.k * CH;  // rows of the chunk inside the context
+    float p[GP][VIT];
 #pragma unroll
     for (int h = 0; h < GP; ++h) {
-      const float a = read_lane(alpha_r[h & 3], 16 * (h >> 2));
+      // scores of this lane's rows: the piece's dot product summed over the row's lanes
+      float mx = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[h][e] *= a;
+      for (int it = 0; it < VIT; ++it) {
+        const float d = piece_sum<DCH>(dot_piece(buf.q[h], buf.k[it]));
+        p[h][it] = (it * TPI + sub < valid) ? d * scale_log2 : -INFINITY;
+        mx = fmaxf(mx, p[h][it]);
+      }
+      // online softmax: the chunk's row 0 is valid, so m_new is finite
+      const float m_new = fmaxf(m[h], token_max<DCH>(mx));
+      const float alpha = __builtin_amdgcn_exp2f(m[h] - m_new);
+      m[h] = m_new;
+      float sum = 0.f;
+#pragma unroll
+      for (int it = 0; it < VIT; ++it) {
+        p[h][it] = __builtin_amdgcn_exp2f(p[h][it] - m_new);
+        sum += p[h][it];
+      }
+      l[h] = l[h] * alpha + sum;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[h][e] *= alpha;
     }
+    // P.V: this lane's rows' V pieces, weighted, into every head's output
 #pragma unroll
     for (int it = 0; it < VIT; ++it) {
-      const int tl = it * TPI + v_sub;
-      float p[GP];
-      if constexpr (GP >= 4) {
-#pragma unroll
-        for (int h4 = 0; h4 < GP; h4 += 4) {
-          const f32x4_t pv = *reinterpret_cast<const f32x4_t*>(&p_lds[wave][tl][h4]);
-          p[h4] = pv[0];
-          p[h4 + 1] = pv[1];
-          p[h4 + 2] = pv[2];
-          p[h4 + 3] = pv[3];
-        }
-      } else {
-#pragma unroll
-        for (int h = 0; h < GP; ++h) p[h] = p_lds[wave][tl][h];
-      }
       float v[8];
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
@@ -384,10 +380,8 @@ __global__ __launch_bounds__(256) void paged_decode_bf16_kernel(
 #pragma unroll
       for (int h = 0; h < GP; ++h)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[h][e] += p[h] * v[e];
+        for (int e = 0; e < 8; ++e) o[h][e] += p[h][it] * v[e];
     }
-    // p_lds[wave] is rewritten by the next chunk: keep these reads before those writes
-    __builtin_amdgcn_wave_barrier();
   };
 
   // End of a segment (x is its last chunk): the final output if the whole stream ran
@@ -396,28 +390,18 @@ __global__ __launch_bounds__(256) void paged_decode_bf16_kernel(
     const int kvh = n_hg == 1 ? x.j : x.j / n_hg;
     const int hg = x.j - kvh * n_hg;
     const int nh = min(GP, G - hg * GP);
-    // reduce over the lanes sharing a head_dim piece
-#pragma unroll
-    for (int h = 0; h < GP; ++h)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float t = o[h][e];
-#pragma unroll
-        for (int sft = DCH; sft < 64; sft <<= 1) t += __shfl_xor(t, sft, 64);
-        o[h][e] = t;
-      }
-    float l_h[GP], m_h[GP];
-#pragma unroll
-    for (int r = 0; r < RR; ++r) l_r[r] = row16_sum(l_r[r]);
+    // sum the shares of the lanes holding the same head_dim piece
+    float l_h[GP];
 #pragma unroll
     for (int h = 0; h < GP; ++h) {
-      l_h[h] = read_lane(l_r[h & 3], 16 * (h >> 2));
-      m_h[h] = read_lane(m_r[h & 3], 16 * (h >> 2));
+      l_h[h] = token_sum<DCH>(l[h]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[h][e] = token_sum<DCH>(o[h][e]);
     }
     const int64_t hq0 = static_cast<int64_t>(x.b) * Hq + kvh * G + hg * GP;
     if (seg_k0 == 0 && x.k == x.nch - 1) {
       // the whole stream ran here: final output
-      if (v_sub == 0) {
+      if (sub == 0) {
 #pragma unroll
         for (int h = 0; h < GP; ++h) {
           if (h >= nh) break;
@@ -426,25 +410,25 @@ __global__ __launch_bounds__(256) void paged_decode_bf16_kernel(
 #pragma unroll
           for (int e2 = 0; e2 < 4; ++e2)
             w[e2] = pack_bf16x2(o[h][2 * e2] * inv, o[h][2 * e2 + 1] * inv);
-          *reinterpret_cast<u32x4_t*>(out + (hq0 + h) * D + v_chunk * 8) = w;
+          *reinterpret_cast<u32x4_t*>(out + (hq0 + h) * D + piece * 8) = w;
         }
       }
     } else {
       const int64_t slot = 2 * static_cast<int64_t>(worker) + (first_segment ? 0 : 1);
-      if (v_sub == 0) {
+      if (sub == 0) {
 #pragma unroll
         for (int h = 0; h < GP; ++h) {
-          float* dst = ws_o + (slot * GP + h) * D + v_chunk * 8;
+          float* dst = ws_o + (slot * GP + h) * D + piece * 8;
           *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{o[h][0], o[h][1], o[h][2], o[h][3]};
           *reinterpret_cast<f32x4_t*>(dst + 4) = f32x4_t{o[h][4], o[h][5], o[h][6], o[h][7]};
         }
       }
       if (lane < GP) {
-        float mm = m_h[0], ll = l_h[0];
+        float mm = m[0], ll = l_h[0];
 #pragma unroll
         for (int h = 1; h < GP; ++h)
           if (lane == h) {
-            mm = m_h[h];
+            mm = m[h];
             ll = l_h[h];
           }
         ws_ml[slot * GP + lane] = make_float2(mm, ll);
@@ -527,13 +511,15 @@ int auto_workers() {
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu, reinterpret_cast<const void*>(&paged_decode_bf16_kernel<D, GP, ONE_BLOCK>), 256, 0) !=
-          hipSuccess ||
+          &per_cu, reinterpret_cast<const void*>(&paged_decode_bf16_kernel<D, GP, ONE_BLOCK>), 256,
+          0) != hipSuccess ||
       cus <= 0 || per_cu <= 0) {
     cus = 256;
     per_cu = 2;
   }
-  w = std::min(kMaxAutoWorkers, cus * per_cu * 4);
+  // at most two waves per SIMD (more measured slower), a whole number of workgroups
+  // per CU (keeps the CUs evenly loaded)
+  w = std::min(kMaxAutoWorkers, cus * std::min(per_cu, 2) * 4);
   cached[dev].store(w, std::memory_order_relaxed);
   return w;
 }
@@ -552,8 +538,8 @@ hipError_t launch_decode(const void* q, void* out, const void* k_cache, const vo
   const DecodeWorkspace ws = carve_decode_workspace(workspace, batch, W, GP);
   const float scale_log2 = scale * kLog2e;
   timing_begin("paged_decode", stream);
-  hipLaunchKernelGGL((paged_decode_bf16_kernel<D, GP, ONE_BLOCK>), dim3((W + 3) / 4), dim3(256), 0,
-                     stream, static_cast<const uint16_t*>(q), static_cast<uint16_t*>(out),
+  hipLaunchKernelGGL((paged_decode_bf16_kernel<D, GP, ONE_BLOCK>), dim3((W + 3) / 4), dim3(256),
+                     0, stream, static_cast<const uint16_t*>(q), static_cast<uint16_t*>(out),
                      static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache),
                      context_lens, block_tables, table_stride, batch, num_q_heads, num_kv_heads,
                      G, n_hg, bs_log2, scale_log2, W, ws.prefix, ws.ml, ws.o);
@@ -578,18 +564,18 @@ hipError_t launch_paged_decode_bf16(int head_dim, const void* q, void* out, cons
                                     int bs_log2, int batch, const int32_t* context_lens,
                                     const int32_t* block_tables, int table_stride, float scale,
                                     int num_workers, void* workspace, hipStream_t stream) {
-  // ONE_BLOCK: every 16-token chunk lies in one block (block_size >= 16)
+  // ONE_BLOCK: every chunk lies in one block (block_size >= the chunk)
   const int GP = heads_per_stream(num_q_heads / num_kv_heads);
-#define PKV_DEC(D_, GP_)                                                                    \
-  return bs_log2 >= 4                                                                       \
-             ? launch_decode<D_, GP_, true>(q, out, k_cache, v_cache, num_q_heads,          \
-                                            num_kv_heads, bs_log2, batch, context_lens,      \
-                                            block_tables, table_stride, scale, num_workers,  \
-                                            workspace, stream)                               \
-             : launch_decode<D_, GP_, false>(q, out, k_cache, v_cache, num_q_heads,         \
-                                             num_kv_heads, bs_log2, batch, context_lens,     \
-                                             block_tables, table_stride, scale, num_workers, \
-                                             workspace, stream)
+#define PKV_DEC(D_, GP_)                                                                 \
+  return (1 << bs_log2) >= kDecodeChunk                                                  \
+             ? launch_decode<D_, GP_, true>(q, out, k_cache, v_cache, num_q_heads,       \
+                                            num_kv_heads, bs_log2, batch, context_lens,   \
+                                            block_tables, table_stride, scale,            \
+                                            num_workers, workspace, stream)               \
+             : launch_decode<D_, GP_, false>(q, out, k_cache, v_cache, num_q_heads,      \
+                                             num_kv_heads, bs_log2, batch, context_lens,  \
+                                             block_tables, table_stride, scale,           \
+                                             num_workers, workspace, stream)
   if (head_dim == 128) {
     switch (GP) {
       case 1: PKV_DEC(128, 1);

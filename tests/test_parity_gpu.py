@@ -158,6 +158,17 @@ def test_rerun_deterministic(pkv):
     assert np.array_equal(a["decode"], b["decode"])
 
 
+def test_decode_large_batch_short_contexts(pkv):
+    """4200 sequences with short ragged contexts (1 to 39 tokens, most inside one
+    16-token chunk): the decode's sequence scan spans many 64-sequence groups and
+    most workers start and end inside tiny streams.  MHA head_dim 64."""
+    rng = np.random.default_rng(21)
+    S = workloads.SeqSpec
+    seqs = [S("decode", int(L), 1) for L in rng.integers(1, 40, size=4200)]
+    wl = workloads.custom("decode_4200", "bf16", 2, 2, 64, 16, seqs, seed=21)
+    _check_outputs(wl, _step(wl), oracle.run_step(wl))
+
+
 @pytest.mark.parametrize("workers", [1, 2, 3, 7, 61, 1000])
 def test_worker_count_agrees(pkv, workers):
     """Any division of the chunk list among workers (1 = every stream whole on one
