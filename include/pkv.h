@@ -108,10 +108,12 @@ pkv_status pkv_paged_prefill(const pkv_cache* cache, const void* q, void* out,
 
 /* Bytes of device workspace pkv_paged_decode needs for this shape; num_workers as
  * in pkv_paged_decode.  0 for the fp32 path (it needs none) and for invalid
- * arguments.  For bf16: 2*W*GP*(4*head_dim + 8) + 8*(batch + 1) bytes, rounded up
- * to 256-byte pieces, with W = num_workers (4096 when 0) and GP = q heads per kv
- * head rounded up to a power of two, at most 8 (about 4.3 MB at GP 1, head_dim 128
- * and W = 4096).  max_context_len does not change it. */
+ * arguments.  For bf16: 2*W*HS*(4*head_dim + 8) + 8*(batch + 1) bytes, rounded up
+ * to 256-byte pieces, with W = num_workers (4096 when 0) and HS = MH*GP heads per
+ * stream (see num_workers): GP = q heads per kv head rounded up to a power of two,
+ * at most 8; MH = the largest power of two dividing num_kv_heads with
+ * MH*head_dim*2 <= 512 (about 8.6 MB at head_dim 128, 32 q / 32 kv heads and
+ * W = 4096).  max_context_len does not change it. */
 size_t pkv_paged_decode_workspace_size(const pkv_cache* cache, int32_t num_q_heads,
                                        int32_t batch, int32_t max_context_len,
                                        int32_t num_workers);
@@ -126,13 +128,14 @@ size_t pkv_paged_decode_workspace_size(const pkv_cache* cache, int32_t num_q_hea
  *   workspace       device scratch of at least
  *                   pkv_paged_decode_workspace_size(...) bytes (may be NULL when
  *                   that size is 0); contents on entry are ignored
- *   num_workers     bf16: the K/V stream of every (sequence, kv head) is cut into
- *                   16-token chunks and the list of all chunks is divided evenly
- *                   among this many wavefront workers; a (sequence, kv head) cut
- *                   between workers is merged exactly (log-sum-exp) by a second
- *                   kernel.  0 = as many workers as the device holds resident
- *                   (at most 4096); W in [1, 2^20] = exactly W (1 = no cut at all).
- *                   Ignored by the fp32 path, which never cuts.
+ *   num_workers     bf16: a stream is (sequence, MH adjacent kv heads, up to GP q
+ *                   heads of each); its K/V is cut into chunks of 2048/(head_dim*MH)
+ *                   tokens, and the list of all chunks is divided evenly among this
+ *                   many wavefront workers; a stream cut between workers is merged
+ *                   exactly (log-sum-exp) by a second kernel.  0 = one worker per
+ *                   SIMD for GP <= 2 and two for larger GP (at most 4096); W in
+ *                   [1, 2^20] = exactly W (1 = no cut at all).  Ignored by the fp32
+ *                   path, which never cuts.
  * The cut depends only on lengths and the worker count, never on block ids, so
  * results are bit-identical under any relabelling of physical blocks. */
 pkv_status pkv_paged_decode(const pkv_cache* cache, const void* q, void* out,

@@ -8,7 +8,8 @@ Decode", "Preparing for computation"):
 * ``paged_prefill``  - varlen causal attention over packed sequences, K/V read
   from the cache through block tables (cached prefix blocks included);
 * ``paged_decode``   - one query per sequence over its cached context, streamed
-  by wavefront workers over 16-token chunks and merged where a context is cut.
+  by wavefront workers over chunks of several kv heads' rows and merged where a
+  context is cut.
 
 This module only marshals arguments: shapes, dtypes and devices are checked,
 pointers and torch's current stream are handed to the C ABI, and every step of

@@ -1,10 +1,11 @@
 // The decode's division of work, shared by the streaming kernel and the merge
-// kernel (internal).  A stream is (sequence, kv head, group of up to GP q heads of
-// that kv head); it is cut into chunks of kDecodeChunk tokens.  All chunks of all
-// streams, in (sequence, stream, position) order, form one list of C chunks; worker
-// w (a wavefront) takes chunks [w*C/W, (w+1)*C/W).  A worker's first segment (its
-// run of chunks of one stream) leaves its partial, if any, in slot 2w, any later one
-// in slot 2w+1; a stream that all falls to one worker is written out directly.
+// kernel (internal).  A stream is (sequence, group of MH adjacent kv heads, group of
+// up to GP q heads of each of those kv heads); it is cut into chunks of
+// chunk_tokens(D, MH) tokens.  All chunks of all streams, in (sequence, stream,
+// position) order, form one list of C chunks; worker w (a wavefront) takes chunks
+// [w*C/W, (w+1)*C/W).  A worker's first segment (its run of chunks of one stream)
+// leaves its partial, if any, in slot 2w, any later one in slot 2w+1; a stream that
+// all falls to one worker is written out directly.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -13,40 +14,55 @@
 
 namespace pkv {
 
-constexpr int kDecodeChunk = 16;       // tokens per chunk
 constexpr int kMaxAutoWorkers = 4096;  // bound on the automatic worker count
 
-// q heads per stream for Hq / Hkv = G: G rounded up to a power of two, at most 8
+// q heads per kv head in a stream for Hq / Hkv = G: G rounded up to a power of two,
+// at most 8
 inline int heads_per_stream(int G) { return G >= 8 ? 8 : (G >= 4 ? 4 : (G >= 2 ? 2 : 1)); }
+
+// kv heads per stream: the largest power of two that divides Hkv and spans at most
+// 512 contiguous bytes of a token's row (2 at head_dim 128, 4 at 64).  Measured on
+// the decode: 512 bytes per token beat 256 and 1 KB (whose 4-token chunks cost more
+// per byte).
+inline int kv_heads_per_stream(int D, int Hkv) {
+  int mh = 1;
+  while (mh * 2 * D * 2 <= 512 && Hkv % (mh * 2) == 0) mh *= 2;
+  return mh;
+}
+
+// Tokens per chunk: four 1 KB load instructions of K (and four of V) per lane group,
+// i.e. 8 KB of K and V per chunk
+__host__ __device__ constexpr int chunk_tokens(int D, int MH) { return 2048 / (D * MH); }
 
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 // Workspace: int64 [batch+1] first chunk of each sequence (the last entry is C),
-// then float2 [2W][GP] (max, sum) and float [2W][GP][D] unnormalised outputs.
+// then float2 [2W][HS] (max, sum) and float [2W][HS][D] unnormalised outputs, HS =
+// MH * GP heads per stream.
 struct DecodeWorkspace {
   int64_t* prefix;
   float2* ml;
   float* o;
 };
-inline DecodeWorkspace carve_decode_workspace(void* ws, int batch, int W, int GP) {
+inline DecodeWorkspace carve_decode_workspace(void* ws, int batch, int W, int HS) {
   char* base = static_cast<char*>(ws);
   DecodeWorkspace d;
   d.prefix = reinterpret_cast<int64_t*>(base);
   base += align256(sizeof(int64_t) * (static_cast<size_t>(batch) + 1));
   d.ml = reinterpret_cast<float2*>(base);
-  base += align256(sizeof(float2) * 2 * static_cast<size_t>(W) * GP);
+  base += align256(sizeof(float2) * 2 * static_cast<size_t>(W) * HS);
   d.o = reinterpret_cast<float*>(base);
   return d;
 }
-inline size_t decode_workspace_bytes(int batch, int W, int GP, int D) {
+inline size_t decode_workspace_bytes(int batch, int W, int HS, int D) {
   return align256(sizeof(int64_t) * (static_cast<size_t>(batch) + 1)) +
-         align256(sizeof(float2) * 2 * static_cast<size_t>(W) * GP) +
-         sizeof(float) * 2 * static_cast<size_t>(W) * GP * D;
+         align256(sizeof(float2) * 2 * static_cast<size_t>(W) * HS) +
+         sizeof(float) * 2 * static_cast<size_t>(W) * HS * D;
 }
 
-// chunks of a sequence of length L
-__device__ __forceinline__ int chunks_of(int L) {
-  return (max(L, 0) + kDecodeChunk - 1) / kDecodeChunk;
+// chunks of 2^ch_log2 tokens in a sequence of length L
+__device__ __forceinline__ int chunks_of(int L, int ch_log2) {
+  return (max(L, 0) + (1 << ch_log2) - 1) >> ch_log2;
 }
 
 // first chunk of worker w
@@ -60,8 +76,9 @@ __device__ __forceinline__ int64_t worker_of(int64_t c, int64_t C, int64_t W) {
 }
 
 // Merge of the partials of the streams that were cut between workers.
-hipError_t launch_decode_combine(int head_dim, int GP, const DecodeWorkspace& ws, void* out,
-                                 const int32_t* context_lens, int batch, int num_q_heads,
-                                 int num_kv_heads, int num_workers, hipStream_t stream);
+hipError_t launch_decode_combine(int head_dim, int GP, int MH, const DecodeWorkspace& ws,
+                                 void* out, const int32_t* context_lens, int batch,
+                                 int num_q_heads, int num_kv_heads, int num_workers,
+                                 hipStream_t stream);
 
 }  // namespace pkv

@@ -9,30 +9,33 @@
 // The pass is a stream over HBM: every K/V byte is read once, so the design is about
 // keeping loads in flight without gaps, not about arithmetic.
 //
-// Work decomposition.  A "stream" is (sequence, kv head, group of up to GP q heads
-// of that kv head); it is cut into chunks of CH tokens.  All chunks of all streams,
-// in (sequence, stream, position) order, form one list of C chunks that is divided
-// evenly among W independent wavefront workers (worker w takes chunks
-// [w*C/W, (w+1)*C/W)), W being as many waves as the device holds resident.  Each
-// worker walks its range with two register buffers: the K/V loads of chunk c+1 (and
-// the block-table entry of chunk c+2) are issued before chunk c is computed, so HBM
-// sees a continuous stream.  K/V are read with non-temporal loads: they are used
-// once, and streaming them past the caches is what lets the read approach the HBM
-// peak.  The cut depends only on lengths and W, never on block ids.
+// Work decomposition.  A "stream" is (sequence, group of MH adjacent kv heads, group
+// of up to GP q heads of each of them); it is cut into chunks of CH tokens.  All
+// chunks of all streams, in (sequence, stream, position) order, form one list of C
+// chunks that is divided evenly among W independent wavefront workers (worker w
+// takes chunks [w*C/W, (w+1)*C/W)).  Each worker walks its range with two register
+// buffers: the K/V loads of chunk c+1 (and the block-table entry of chunk c+2) are
+// issued before chunk c is computed, so HBM sees a continuous stream.  K/V are read
+// with non-temporal loads: they are used once, and streaming them past the caches is
+// what lets the read approach the HBM peak.  The cut depends only on lengths and W,
+// never on block ids.
 //
-// Per chunk and worker, K and V are read alike: lane (sub, piece) loads 16 bytes,
-// piece `piece` of one row, so each load instruction covers whole rows (whole
-// 128-byte lines, the access pattern HBM streams fastest).  Then, on the vector ALU:
-//   * scores: per head, the q piece . K piece (bf16 pair dot products, fp32
-//     accumulation), summed over the row's lanes with DPP moves; every grouped q head
-//     reuses each K row loaded;
+// Per chunk and worker, K and V are read alike: lane (sub, hh, piece) loads 16 bytes,
+// piece `piece` of kv head hh in row `sub` of the instruction, so each load
+// instruction covers whole head rows of MH adjacent heads: MH*2*D contiguous bytes of
+// each token row it touches (MH is chosen for 512 bytes, the size measured to stream
+// best).  Then, on the vector ALU:
+//   * scores: per q head, the q piece . K piece (bf16 pair dot products, fp32
+//     accumulation), summed over the head row's lanes with DPP moves; every grouped q
+//     head reuses each K row loaded;
 //   * online softmax in the log2 domain (scale * log2 e folded into one multiply):
-//     max over the chunk's rows with DPP and v_permlane16/32_swap, exp2, per-lane
-//     shares of the row sum;
+//     max over the chunk's rows in-lane and, across the rows one instruction spreads
+//     over lanes, with v_permlane16/32_swap; exp2; per-lane shares of the row sum;
 //   * P.V: each lane accumulates its rows' weighted V pieces; the lanes holding one
-//     head_dim piece are summed once, at the end of the segment.
+//     head_dim piece of a head are summed once, at the end of the segment.
+// q changes only with the stream, so it is loaded once per segment.
 // Rows past context_len are never read: the buffer loads' range check returns zeros
-// for them (block_size >= 16), or they re-read the chunk's last valid row (smaller
+// for them (block_size >= CH), or they re-read the chunk's last valid row (smaller
 // blocks), so neither the stale tail of the last block nor a table entry past it is
 // ever touched; their scores are masked to -inf.
 //
@@ -97,20 +100,18 @@ struct Cursor {
   int b;    // sequence
   int L;    // its context length
   int nch;  // its chunks per stream
-  int j;    // stream within the sequence: kv head * n_hg + head group
+  int j;    // stream within the sequence: kv head group * n_hg + q head group
   int k;    // chunk within the stream
 };
 
-// One chunk's operands in registers, K and V alike: lane (token, 16-byte piece) as
-// in a whole-row load (every load instruction covers whole rows: whole 128-byte
-// lines, the pattern HBM streams fastest), plus this lane's piece of each q row of
-// the stream.
-template <int D, int CH, int GP>
+// Loads per lane per chunk, for K and for V alike (each one 16 bytes)
+constexpr int kChunkLoads = 4;
+
+// One chunk's operands in registers: this lane's 16-byte pieces of K and V, one per
+// load instruction.
 struct KVBuf {
-  static constexpr int N = CH * (D / 8) / 64;  // 16-byte pieces per lane (K and V each)
-  u32x4_t k[N];
-  u32x4_t v[N];
-  u32x4_t q[GP];
+  u32x4_t k[kChunkLoads];
+  u32x4_t v[kChunkLoads];
 };
 
 // q . k over one 16-byte piece (8 products as 4 bf16 pair dot products, fp32
@@ -139,33 +140,48 @@ __device__ __forceinline__ float piece_sum(float x) {
   return x;
 }
 
-// Max / sum over the token groups of a wavefront (lanes l, l^8 (half rows, head_dim 64
-// only), l^16, l^32): DPP row_ror:8 and v_permlane16/32_swap, no LDS.
-template <int DCH>
-__device__ __forceinline__ float token_max(float x) {
-  if constexpr (DCH == 8) x = fmaxf(x, dpp<0x128>(x));  // row_ror:8
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+// Max / sum over the lanes that differ only in the bits from STRIDE up (the rows a
+// load instruction spreads over lanes STRIDE apart): DPP row_ror:8 (lanes l and
+// l^8), v_permlane16_swap (l^16) and v_permlane32_swap (l^32); no LDS.  STRIDE = 64:
+// nothing to reduce.
+template <int STRIDE>
+__device__ __forceinline__ float sub_max(float x) {
+  if constexpr (STRIDE <= 8) x = fmaxf(x, dpp<0x128>(x));  // row_ror:8
+  if constexpr (STRIDE <= 16) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  }
+  if constexpr (STRIDE <= 32) {
+    const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    x = fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+  }
+  return x;
 }
-template <int DCH>
-__device__ __forceinline__ float token_sum(float x) {
-  if constexpr (DCH == 8) x += dpp<0x128>(x);  // row_ror:8
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+template <int STRIDE>
+__device__ __forceinline__ float sub_sum(float x) {
+  if constexpr (STRIDE <= 8) x += dpp<0x128>(x);  // row_ror:8
+  if constexpr (STRIDE <= 16) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  }
+  if constexpr (STRIDE <= 32) {
+    const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    x = __uint_as_float(c[0]) + __uint_as_float(c[1]);
+  }
+  return x;
 }
 
 }  // namespace
 
-template <int D, int GP, bool ONE_BLOCK>
-__global__ __launch_bounds__(256) void paged_decode_bf16_kernel(
+// (at least two waves per SIMD: the eight-head groups would otherwise take a few
+// registers past 256 and run one wave per SIMD)
+template <int D, int GP, int MH, bool ONE_BLOCK>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void
+paged_decode_bf16_kernel(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
     const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ block_tables,
@@ -173,13 +189,18 @@ __global__ __launch_bounds__(256) void paged_decode_bf16_kernel(
     float scale_log2, int num_workers, int64_t* __restrict__ ws_prefix,
     float2* __restrict__ ws_ml, float* __restrict__ ws_o) {
   static_assert(D == 64 || D == 128, "head_dim");
-  static_assert(GP == 1 || GP == 2 || GP == 4 || GP == 8, "heads per stream");
-  constexpr int CH = kDecodeChunk;
-  static_assert(CH == 16 || CH == 32, "chunk");
-  constexpr int DCH = D / 8;     // 16-byte pieces per row
-  constexpr int TPI = 64 / DCH;  // rows per load instruction
-  constexpr int VIT = CH / TPI;  // K (and V) loads per lane per chunk
-  typedef KVBuf<D, CH, GP> Buf;
+  static_assert(GP == 1 || GP == 2 || GP == 4 || GP == 8, "q heads per kv head in a stream");
+  constexpr int DCH = D / 8;         // 16-byte pieces per head row
+  constexpr int HPI = 64 / DCH;      // head rows per load instruction
+  static_assert(MH >= 1 && MH <= HPI && (MH & (MH - 1)) == 0, "kv heads per stream");
+  constexpr int TPI = HPI / MH;      // tokens per load instruction
+  constexpr int VIT = kChunkLoads;   // K (and V) loads per lane per chunk
+  constexpr int CH = VIT * TPI;      // tokens per chunk
+  static_assert(CH == chunk_tokens(D, MH), "chunk");
+  constexpr int CH_LOG2 = CH == 32 ? 5 : CH == 16 ? 4 : CH == 8 ? 3 : 2;
+  constexpr int SUB = DCH * MH;      // lane stride between the tokens of an instruction
+  constexpr int HS = MH * GP;        // heads of a stream's partials
+  typedef KVBuf Buf;
 
   // wave index through readfirstlane: the compiler then knows everything derived
   // from it (the worker's chunk range and cursor) is wavefront-uniform
@@ -187,9 +208,12 @@ __global__ __launch_bounds__(256) void paged_decode_bf16_kernel(
   const int lane = threadIdx.x & 63;
   const int worker = blockIdx.x * 4 + wave;
   if (worker >= num_workers) return;  // wavefront-uniform; the kernel has no block barrier
-  const int piece = lane % DCH;  // 16-byte piece of a row: head_dim [8*piece, 8*piece+8)
-  const int sub = lane / DCH;    // row within a load instruction
-  const int S = Hkv * n_hg;
+  // lane = (sub * MH + hh) * DCH + piece: 16-byte piece `piece` (head_dim
+  // [8*piece, 8*piece+8)) of kv head hh of the stream, token `sub` of the instruction
+  const int piece = lane % DCH;
+  const int hh = (lane / DCH) % MH;
+  const int sub = lane / SUB;
+  const int S = (Hkv / MH) * n_hg;
   const int bs_mask = (1 << bs_log2) - 1;
   const uint32_t row_bytes = static_cast<uint32_t>(Hkv) * D * 2;  // token stride in a block
 
@@ -197,7 +221,7 @@ __global__ __launch_bounds__(256) void paged_decode_bf16_kernel(
   // also records every sequence's first chunk for the combine kernel.
   int64_t tot = 0;
   for (int b0 = 0; b0 < batch; b0 += 64)
-    if (b0 + lane < batch) tot += static_cast<int64_t>(chunks_of(context_lens[b0 + lane])) * S;
+    if (b0 + lane < batch) tot += static_cast<int64_t>(chunks_of(context_lens[b0 + lane], CH_LOG2)) * S;
   const int64_t C = read_lane64(wave_sum64(tot), 0);
   const int64_t W = num_workers;
   const int64_t c_begin = worker * C / W;
@@ -208,7 +232,7 @@ __global__ __launch_bounds__(256) void paged_decode_bf16_kernel(
     int64_t carry = 0;
     for (int b0 = 0; b0 < batch; b0 += 64) {
       const int b = b0 + lane;
-      const int64_t n = b < batch ? static_cast<int64_t>(chunks_of(context_lens[b])) * S : 0;
+      const int64_t n = b < batch ? static_cast<int64_t>(chunks_of(context_lens[b], CH_LOG2)) * S : 0;
       int64_t incl = n;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
@@ -235,7 +259,7 @@ __global__ __launch_bounds__(256) void paged_decode_bf16_kernel(
   Cursor cur;
   cur.b = b_first;
   cur.L = context_lens[b_first];
-  cur.nch = chunks_of(cur.L);
+  cur.nch = chunks_of(cur.L, CH_LOG2);
   {
     const int64_t r = c_begin - p_first;
     cur.j = static_cast<int>(r / cur.nch);
@@ -249,7 +273,7 @@ __global__ __launch_bounds__(256) void paged_decode_bf16_kernel(
         do {  // the list holds a later chunk, so a sequence with chunks follows
           ++x.b;
           x.L = context_lens[x.b];
-          x.nch = chunks_of(x.L);
+          x.nch = chunks_of(x.L, CH_LOG2);
         } while (x.nch == 0);
       }
     }
@@ -264,39 +288,57 @@ __global__ __launch_bounds__(256) void paged_decode_bf16_kernel(
     const int tok = min(x.k * CH + (lane & (CH - 1)), x.L - 1);
     return block_tables[static_cast<int64_t>(x.b) * table_stride + (tok >> bs_log2)];
   };
-  // Lane (sub, piece) reads piece `piece` of rows it*TPI + sub.  Every load of a chunk
-  // is issued without a condition, so the compiler's waits count them in order.
-  // With ONE_BLOCK the chunk lies in one block and K, V and q are read with buffer
-  // loads: a wavefront-uniform descriptor (base = the chunk's first row) plus the
+  // Lane (sub, hh, piece) reads piece `piece` of kv head hh of the stream in rows
+  // it*TPI + sub: each load instruction covers TPI rows of MH heads, 1 KB of
+  // contiguous row bytes when MH = HPI.  Every load of a chunk is issued without a
+  // condition, so the compiler's waits count them in order.  With ONE_BLOCK the chunk
+  // lies in one block and K, V (and q) are read with buffer loads: a wavefront-uniform
+  // descriptor (base = the stream's first head in the chunk's first row) plus the
   // loop-invariant 32-bit lane offsets `kv_off`, so issuing writes no vector register
   // but the load destinations (a vector temporary there would make the compiler wait
-  // for loads still in flight).  The descriptor's size ends at the context: rows past
-  // it (the stale tail of the last block) come back as zeros without a memory access,
-  // and so do q rows past the stream's heads.  Without ONE_BLOCK a chunk spans several
-  // blocks: rows past the context re-read the chunk's last valid row (their weight is
-  // exactly 0) and q rows past the stream's heads re-read its first row (those heads
-  // are never written out).  A `live` == false chunk (the one after a worker's last)
-  // repeats the worker's last chunk.
+  // for loads still in flight).  The descriptor's size ends with the context's last
+  // row: rows past it (the stale tail of the last block) come back as zeros without a
+  // memory access.  Without ONE_BLOCK a chunk spans several blocks: rows past the
+  // context re-read the chunk's last valid row (their weight is exactly 0).  A `live`
+  // == false chunk (the one after a worker's last) repeats the worker's last chunk.
   uint32_t kv_off[VIT];
 #pragma unroll
   for (int it = 0; it < VIT; ++it)
-    kv_off[it] = static_cast<uint32_t>(it * TPI + sub) * row_bytes + piece * 16;
-  auto issue = [&](const Cursor& x, int te, Buf& buf, bool live) {
-    const int kvh = n_hg == 1 ? x.j : x.j / n_hg;
-    const int hg = x.j - kvh * n_hg;
-    const int tok0 = x.k * CH;
+    kv_off[it] = static_cast<uint32_t>(it * TPI + sub) * row_bytes + hh * D * 2 + piece * 16;
+  const uint32_t q_off = static_cast<uint32_t>(hh * G * D * 2 + piece * 16);
+  // this lane's pieces of the q rows of x's stream (kv head hh, q heads g < GP; rows
+  // past the group's heads re-read its last one, and those heads are never written
+  // out).  Loaded once per segment, in order between the loads of its first chunk
+  // and those of the chunk after, so the wait for them is the wait for that chunk.
+  u32x4_t qv[GP];
+  auto load_q = [&](const Cursor& x) {
+    const int kvg = n_hg == 1 ? x.j : x.j / n_hg;
+    const int hg = x.j - kvg * n_hg;
     const int nh = min(GP, G - hg * GP);
-    const uint16_t* qb = q + (static_cast<int64_t>(x.b) * Hq + kvh * G + hg * GP) * D;
+    const int qrow0 = kvg * MH * G + hg * GP;  // this lane's q rows: qrow0 + hh*G + g
+    if constexpr (ONE_BLOCK) {
+      const auto qr = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(q + static_cast<int64_t>(x.b) * Hq * D), 0, Hq * D * 2,
+          kBufferWord3);
+#pragma unroll
+      for (int g = 0; g < GP; ++g)
+        qv[g] = __builtin_amdgcn_raw_buffer_load_b128(qr, q_off, (qrow0 + min(g, nh - 1)) * D * 2,
+                                                      0);
+    } else {
+      const uint16_t* qb = q + (static_cast<int64_t>(x.b) * Hq + qrow0 + hh * G) * D + piece * 8;
+#pragma unroll
+      for (int g = 0; g < GP; ++g)
+        qv[g] = *reinterpret_cast<const u32x4_t*>(qb + min(g, nh - 1) * D);
+    }
+  };
+  auto issue = [&](const Cursor& x, int te, Buf& buf, bool live) {
+    const int kv0 = (n_hg == 1 ? x.j : x.j / n_hg) * MH;  // the stream's first kv head
+    const int tok0 = x.k * CH;
     if constexpr (ONE_BLOCK) {
       (void)live;
-      const auto qr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(qb), 0, nh * D * 2,
-                                                        kBufferWord3);
-#pragma unroll
-      for (int h = 0; h < GP; ++h)
-        buf.q[h] = __builtin_amdgcn_raw_buffer_load_b128(qr, piece * 16 + h * D * 2, 0, 0);
       const int64_t blk = __builtin_amdgcn_readfirstlane(te);
-      const int64_t first = ((blk << bs_log2) | (tok0 & bs_mask)) * Hkv + kvh;
-      const int bytes = min(x.L - tok0, CH) * static_cast<int>(row_bytes);
+      const int64_t first = ((blk << bs_log2) | (tok0 & bs_mask)) * Hkv + kv0;
+      const int bytes = (min(x.L - tok0, CH) - 1) * static_cast<int>(row_bytes) + MH * D * 2;
       const auto kr = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<uint16_t*>(k_cache + first * D), 0, bytes, kBufferWord3);
       const auto vr = __builtin_amdgcn_make_buffer_rsrc(
@@ -307,25 +349,22 @@ __global__ __launch_bounds__(256) void paged_decode_bf16_kernel(
         buf.v[it] = __builtin_amdgcn_raw_buffer_load_b128(vr, kv_off[it], 0, kNonTemporal);
       }
     } else {
-#pragma unroll
-      for (int h = 0; h < GP; ++h)
-        buf.q[h] = *reinterpret_cast<const u32x4_t*>(qb + (h < nh ? h : 0) * D + piece * 8);
       const int last = live ? min(x.L - tok0, CH) - 1 : 0;  // last row read
 #pragma unroll
       for (int it = 0; it < VIT; ++it) {
         const int tl = min(it * TPI + sub, last);
         const int64_t off =
-            token_row(__shfl(te, tl, 64), tok0 + tl, bs_log2, Hkv, kvh, D) + piece * 8;
+            token_row(__shfl(te, tl, 64), tok0 + tl, bs_log2, Hkv, kv0 + hh, D) + piece * 8;
         buf.k[it] = load_stream(k_cache + off);
         buf.v[it] = load_stream(v_cache + off);
       }
     }
   };
 
-  // Running softmax state of the current segment, per head: the max m (log2 domain,
-  // the same in every lane), this lane's share of the sum (its rows' weights; the
-  // lanes of one row hold equal shares) and of the unnormalised output (its rows,
-  // head_dim [8*piece, 8*piece+8)).
+  // Running softmax state of the current segment, per q head g of this lane's kv head:
+  // the max m (log2 domain, the same in every lane of the kv head), this lane's share
+  // of the sum (its rows' weights; the lanes of one row hold equal shares) and of the
+  // unnormalised output (its rows, head_dim [8*piece, 8*piece+8)).
   float m[GP], l[GP], o[GP][8];
   auto reset = [&]() {
 #pragma unroll
@@ -350,12 +389,12 @@ __global__ __launch_bounds__(256) void paged_decode_bf16_kernel(
       float mx = -INFINITY;
 #pragma unroll
       for (int it = 0; it < VIT; ++it) {
-        const float d = piece_sum<DCH>(dot_piece(buf.q[h], buf.k[it]));
+        const float d = piece_sum<DCH>(dot_piece(qv[h], buf.k[it]));
         p[h][it] = (it * TPI + sub < valid) ? d * scale_log2 : -INFINITY;
         mx = fmaxf(mx, p[h][it]);
       }
       // online softmax: the chunk's row 0 is valid, so m_new is finite
-      const float m_new = fmaxf(m[h], token_max<DCH>(mx));
+      const float m_new = fmaxf(m[h], sub_max<SUB>(mx));
       const float alpha = __builtin_amdgcn_exp2f(m[h] - m_new);
       m[h] = m_new;
       float sum = 0.f;
@@ -387,21 +426,21 @@ __global__ __launch_bounds__(256) void paged_decode_bf16_kernel(
   // End of a segment (x is its last chunk): the final output if the whole stream ran
   // on this worker, else the worker's partial for the combine kernel.
   auto finalize = [&](const Cursor& x) {
-    const int kvh = n_hg == 1 ? x.j : x.j / n_hg;
-    const int hg = x.j - kvh * n_hg;
+    const int kvg = n_hg == 1 ? x.j : x.j / n_hg;
+    const int hg = x.j - kvg * n_hg;
     const int nh = min(GP, G - hg * GP);
-    // sum the shares of the lanes holding the same head_dim piece
+    // sum the shares of the lanes holding the same head and head_dim piece
     float l_h[GP];
 #pragma unroll
     for (int h = 0; h < GP; ++h) {
-      l_h[h] = token_sum<DCH>(l[h]);
+      l_h[h] = sub_sum<SUB>(l[h]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[h][e] = token_sum<DCH>(o[h][e]);
+      for (int e = 0; e < 8; ++e) o[h][e] = sub_sum<SUB>(o[h][e]);
     }
-    const int64_t hq0 = static_cast<int64_t>(x.b) * Hq + kvh * G + hg * GP;
     if (seg_k0 == 0 && x.k == x.nch - 1) {
       // the whole stream ran here: final output
       if (sub == 0) {
+        const int64_t row0 = static_cast<int64_t>(x.b) * Hq + (kvg * MH + hh) * G + hg * GP;
 #pragma unroll
         for (int h = 0; h < GP; ++h) {
           if (h >= nh) break;
@@ -410,7 +449,7 @@ __global__ __launch_bounds__(256) void paged_decode_bf16_kernel(
 #pragma unroll
           for (int e2 = 0; e2 < 4; ++e2)
             w[e2] = pack_bf16x2(o[h][2 * e2] * inv, o[h][2 * e2 + 1] * inv);
-          *reinterpret_cast<u32x4_t*>(out + (hq0 + h) * D + piece * 8) = w;
+          *reinterpret_cast<u32x4_t*>(out + (row0 + h) * D + piece * 8) = w;
         }
       }
     } else {
@@ -418,20 +457,14 @@ __global__ __launch_bounds__(256) void paged_decode_bf16_kernel(
       if (sub == 0) {
 #pragma unroll
         for (int h = 0; h < GP; ++h) {
-          float* dst = ws_o + (slot * GP + h) * D + piece * 8;
+          float* dst = ws_o + (slot * HS + hh * GP + h) * D + piece * 8;
           *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{o[h][0], o[h][1], o[h][2], o[h][3]};
           *reinterpret_cast<f32x4_t*>(dst + 4) = f32x4_t{o[h][4], o[h][5], o[h][6], o[h][7]};
         }
-      }
-      if (lane < GP) {
-        float mm = m[0], ll = l_h[0];
+        if (piece == 0) {
 #pragma unroll
-        for (int h = 1; h < GP; ++h)
-          if (lane == h) {
-            mm = m[h];
-            ll = l_h[h];
-          }
-        ws_ml[slot * GP + lane] = make_float2(mm, ll);
+          for (int h = 0; h < GP; ++h) ws_ml[slot * HS + hh * GP + h] = make_float2(m[h], l_h[h]);
+        }
       }
     }
     reset();
@@ -451,6 +484,7 @@ __global__ __launch_bounds__(256) void paged_decode_bf16_kernel(
   if (n_chunks > 1) advance(nxt);
   int te_nxt = table_entry(nxt);
   issue(cur, table_entry(cur), bufA, true);
+  load_q(cur);
   bool has_next = false;
   Cursor nn = nxt;
   int te_nn = 0;
@@ -496,12 +530,13 @@ __global__ __launch_bounds__(256) void paged_decode_bf16_kernel(
     nxt = nn;
     te_nxt = te_nn;
     seg_k0 = 0;
+    load_q(cur);  // a new segment is a new stream
   }
 }
 
 namespace {
 
-template <int D, int GP, bool ONE_BLOCK>
+template <int D, int GP, int MH, bool ONE_BLOCK>
 int auto_workers() {
   static std::atomic<int> cached[64];
   int dev = 0;
@@ -511,20 +546,23 @@ int auto_workers() {
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu, reinterpret_cast<const void*>(&paged_decode_bf16_kernel<D, GP, ONE_BLOCK>), 256,
-          0) != hipSuccess ||
+          &per_cu, reinterpret_cast<const void*>(&paged_decode_bf16_kernel<D, GP, MH, ONE_BLOCK>),
+          256, 0) != hipSuccess ||
       cus <= 0 || per_cu <= 0) {
     cus = 256;
     per_cu = 2;
   }
-  // at most two waves per SIMD (more measured slower), a whole number of workgroups
-  // per CU (keeps the CUs evenly loaded)
-  w = std::min(kMaxAutoWorkers, cus * std::min(per_cu, 2) * 4);
+  // Waves per SIMD: one while each byte streamed costs little arithmetic (up to 2 q
+  // heads per kv head), two beyond (the VALU then needs a second wave to hide behind).
+  // Measured: more concurrent streams read HBM less efficiently, so the smallest count
+  // that keeps the arithmetic hidden is the fastest.  A whole number of workgroups per
+  // CU keeps the CUs evenly loaded.
+  w = std::min(kMaxAutoWorkers, cus * std::min(per_cu, GP <= 2 ? 1 : 2) * 4);
   cached[dev].store(w, std::memory_order_relaxed);
   return w;
 }
 
-template <int D, int GP, bool ONE_BLOCK>
+template <int D, int GP, int MH, bool ONE_BLOCK>
 hipError_t launch_decode(const void* q, void* out, const void* k_cache, const void* v_cache,
                          int num_q_heads, int num_kv_heads, int bs_log2, int batch,
                          const int32_t* context_lens, const int32_t* block_tables,
@@ -532,22 +570,58 @@ hipError_t launch_decode(const void* q, void* out, const void* k_cache, const vo
                          hipStream_t stream) {
   const int G = num_q_heads / num_kv_heads;
   const int n_hg = (G + GP - 1) / GP;
-  const int S = num_kv_heads * n_hg;
+  const int S = (num_kv_heads / MH) * n_hg;
   if (S > 65535) return hipErrorInvalidConfiguration;
-  const int W = num_workers > 0 ? num_workers : auto_workers<D, GP, ONE_BLOCK>();
-  const DecodeWorkspace ws = carve_decode_workspace(workspace, batch, W, GP);
+  const int W = num_workers > 0 ? num_workers : auto_workers<D, GP, MH, ONE_BLOCK>();
+  const DecodeWorkspace ws = carve_decode_workspace(workspace, batch, W, MH * GP);
   const float scale_log2 = scale * kLog2e;
   timing_begin("paged_decode", stream);
-  hipLaunchKernelGGL((paged_decode_bf16_kernel<D, GP, ONE_BLOCK>), dim3((W + 3) / 4), dim3(256),
-                     0, stream, static_cast<const uint16_t*>(q), static_cast<uint16_t*>(out),
-                     static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache),
-                     context_lens, block_tables, table_stride, batch, num_q_heads, num_kv_heads,
-                     G, n_hg, bs_log2, scale_log2, W, ws.prefix, ws.ml, ws.o);
+  hipLaunchKernelGGL((paged_decode_bf16_kernel<D, GP, MH, ONE_BLOCK>), dim3((W + 3) / 4),
+                     dim3(256), 0, stream, static_cast<const uint16_t*>(q),
+                     static_cast<uint16_t*>(out), static_cast<const uint16_t*>(k_cache),
+                     static_cast<const uint16_t*>(v_cache), context_lens, block_tables,
+                     table_stride, batch, num_q_heads, num_kv_heads, G, n_hg, bs_log2,
+                     scale_log2, W, ws.prefix, ws.ml, ws.o);
   timing_end(stream);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_decode_combine(D, GP, ws, out, context_lens, batch, num_q_heads, num_kv_heads, W,
-                               stream);
+  return launch_decode_combine(D, GP, MH, ws, out, context_lens, batch, num_q_heads,
+                               num_kv_heads, W, stream);
+}
+
+template <int D, int GP, int MH>
+hipError_t launch_decode_bs(const void* q, void* out, const void* k_cache, const void* v_cache,
+                            int num_q_heads, int num_kv_heads, int bs_log2, int batch,
+                            const int32_t* context_lens, const int32_t* block_tables,
+                            int table_stride, float scale, int num_workers, void* workspace,
+                            hipStream_t stream) {
+  // ONE_BLOCK: every chunk lies in one block (block_size >= the chunk)
+  if ((1 << bs_log2) >= chunk_tokens(D, MH))
+    return launch_decode<D, GP, MH, true>(q, out, k_cache, v_cache, num_q_heads, num_kv_heads,
+                                          bs_log2, batch, context_lens, block_tables,
+                                          table_stride, scale, num_workers, workspace, stream);
+  return launch_decode<D, GP, MH, false>(q, out, k_cache, v_cache, num_q_heads, num_kv_heads,
+                                         bs_log2, batch, context_lens, block_tables,
+                                         table_stride, scale, num_workers, workspace, stream);
+}
+
+template <int D, int MH>
+hipError_t launch_decode_gp(int GP, const void* q, void* out, const void* k_cache,
+                            const void* v_cache, int num_q_heads, int num_kv_heads, int bs_log2,
+                            int batch, const int32_t* context_lens, const int32_t* block_tables,
+                            int table_stride, float scale, int num_workers, void* workspace,
+                            hipStream_t stream) {
+#define PKV_DEC(GP_)                                                                         \
+  return launch_decode_bs<D, GP_, MH>(q, out, k_cache, v_cache, num_q_heads, num_kv_heads, \
+                                      bs_log2, batch, context_lens, block_tables,          \
+                                      table_stride, scale, num_workers, workspace, stream)
+  switch (GP) {
+    case 1: PKV_DEC(1);
+    case 2: PKV_DEC(2);
+    case 4: PKV_DEC(4);
+    default: PKV_DEC(8);
+  }
+#undef PKV_DEC
 }
 
 }  // namespace
@@ -555,7 +629,8 @@ hipError_t launch_decode(const void* q, void* out, const void* k_cache, const vo
 size_t paged_decode_bf16_workspace(int head_dim, int num_q_heads, int num_kv_heads, int batch,
                                    int num_workers) {
   const int GP = heads_per_stream(num_q_heads / num_kv_heads);
-  return decode_workspace_bytes(batch, num_workers > 0 ? num_workers : kMaxAutoWorkers, GP,
+  const int MH = kv_heads_per_stream(head_dim, num_kv_heads);
+  return decode_workspace_bytes(batch, num_workers > 0 ? num_workers : kMaxAutoWorkers, MH * GP,
                                 head_dim);
 }
 
@@ -564,27 +639,20 @@ hipError_t launch_paged_decode_bf16(int head_dim, const void* q, void* out, cons
                                     int bs_log2, int batch, const int32_t* context_lens,
                                     const int32_t* block_tables, int table_stride, float scale,
                                     int num_workers, void* workspace, hipStream_t stream) {
-  // ONE_BLOCK: every chunk lies in one block (block_size >= the chunk)
   const int GP = heads_per_stream(num_q_heads / num_kv_heads);
-#define PKV_DEC(D_, GP_)                                                                 \
-  return (1 << bs_log2) >= kDecodeChunk                                                  \
-             ? launch_decode<D_, GP_, true>(q, out, k_cache, v_cache, num_q_heads,       \
-                                            num_kv_heads, bs_log2, batch, context_lens,   \
-                                            block_tables, table_stride, scale,            \
-                                            num_workers, workspace, stream)               \
-             : launch_decode<D_, GP_, false>(q, out, k_cache, v_cache, num_q_heads,      \
-                                             num_kv_heads, bs_log2, batch, context_lens,  \
-                                             block_tables, table_stride, scale,           \
-                                             num_workers, workspace, stream)
+  const int MH = kv_heads_per_stream(head_dim, num_kv_heads);
+#define PKV_DEC(D_, MH_)                                                                      \
+  return launch_decode_gp<D_, MH_>(GP, q, out, k_cache, v_cache, num_q_heads, num_kv_heads, \
+                                   bs_log2, batch, context_lens, block_tables, table_stride, \
+                                   scale, num_workers, workspace, stream)
   if (head_dim == 128) {
-    switch (GP) {
+    switch (MH) {
       case 1: PKV_DEC(128, 1);
       case 2: PKV_DEC(128, 2);
-      case 4: PKV_DEC(128, 4);
-      default: PKV_DEC(128, 8);
+      default: PKV_DEC(128, 4);
     }
   }
-  switch (GP) {
+  switch (MH) {
     case 1: PKV_DEC(64, 1);
     case 2: PKV_DEC(64, 2);
     case 4: PKV_DEC(64, 4);
