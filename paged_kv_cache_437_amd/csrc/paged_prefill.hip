@@ -20,13 +20,13 @@
 //                                row-major V tile, B = P converted to bf16 in place.
 // The key order inside each MFMA k-step is the same permutation for both operands,
 // so the P registers produced by the S^T MFMA feed the O^T MFMA without shuffles.
-// K/V tiles are double buffered in LDS with rows padded to D + 8 (K) and D + 32 (V)
-// elements, the pitches with the fewest bank conflicts for the 16-byte and the
-// transposing reads; tile j+1 is fetched
-// into registers while tile j is computed.  Keys at or past Lk re-read the tile's
-// last valid key (stale rows never enter; their scores are masked), table entries
-// past the last used block are never read, and causal masking is applied only on
-// tiles that cross the diagonal.
+// K/V tiles are double buffered in LDS and land there straight from global memory
+// (16-byte direct-to-LDS loads: no register staging, no LDS write instructions);
+// tile j+1 is in flight while tile j is computed.  The tiles are unpadded, with a
+// 16-byte chunk swizzle that keeps both operand reads free of bank conflicts.  Keys
+// at or past Lk re-read the tile's last valid key (stale rows never enter; their
+// scores are masked), table entries past the last used block are never read, and
+// causal masking is applied only on tiles that cross the diagonal.
 // Work order: workgroups take the (sequence, kv head, q tile) items by tile rank
 // counted from each sequence's last (heaviest) tile, so long causal tiles start
 // first; the grid is sized for the longest sequence and the slots past the real
@@ -112,6 +112,40 @@ __device__ bool prefill_item(int64_t i, int batch, int Hkv, int bm_tok, int max_
   return false;  // not reached for i inside the list
 }
 
+// 16-byte chunk swizzle of the unpadded LDS K/V tiles (64 banks of 4 bytes: a 256-byte
+// bank line): logical chunk c of row r sits at physical chunk c ^ swz<D>(r).  It puts
+// the 16 rows that the 16 lanes of one ds_read_b128 cycle read (the K operand, one
+// logical chunk) on 16 distinct chunk slots of the bank line, and the 4 rows x 64 bytes
+// that 32 lanes of one transposing-read cycle take (the V operand) on disjoint slots.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+typedef __attribute__((address_space(3))) char lds_char;
+
+// 16 bytes per lane from global memory straight into LDS: lane l's 16 bytes land at
+// LDS byte lds + 16 l.  Issued as inline assembly so the compiler does not track it:
+// the kernel orders these writes against the LDS reads itself (vmcnt(0) and a
+// barrier before a tile is read; a buffer is refilled only after every wave is done
+// with it).
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_char*)p));
+}
+__device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma16_ptr(const void* p, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds), "v"(p)
+               : "memory", "m0");
+}
+
 template <int D, int GP, bool BIG_BLOCK>
 __global__ __launch_bounds__(256, 2) void paged_prefill_bf16_kernel(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
@@ -122,24 +156,24 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_bf16_kernel(
   static_assert(D == 64 || D == 128, "head_dim");
   constexpr int BM_TOK = 128 / GP;  // tokens per workgroup tile
   constexpr int BN = 64;            // keys per K/V tile
-  // LDS row pitches (elements).  K is read 16 bytes per lane, one row per lane: a pitch
-  // of D + 8 puts 16 consecutive rows on distinct banks.  V is read 8 bytes per lane by
-  // the transposing reads, 4 rows x 64 bytes per half-wave: a pitch of D + 32 spreads
-  // those rows (both measured fastest among D + 0/8/16/32 on gfx950).
-  constexpr int KPK = D + 8;
-  constexpr int KPV = D + 32;
+  constexpr int RB = D * 2;         // bytes per LDS row (unpadded)
+  constexpr int TB = BN * RB;       // bytes per LDS tile
   constexpr int KS = D / 16;        // S^T MFMA k-steps over head_dim
   constexpr int DT = D / 32;        // O^T tiles of 32 head_dim rows
   constexpr int CPR = D / 8;        // 16-byte chunks per K/V row
-  constexpr int RPI = 256 / CPR;    // rows per workgroup load instruction
-  constexpr int LIT = BN / RPI;     // load instructions per tile (K and V each)
+  constexpr int RPL = 64 / CPR;     // rows per wavefront load instruction (1 KB)
+  constexpr int LIT = BN / (4 * RPL);  // load instructions per wavefront per tile (K and V each)
   // Lazy rescaling: the running max a row's probabilities are taken against moves
   // only when a new score exceeds it by more than 2^8 (log2 domain), so most tiles
   // skip the rescale of the accumulators; probabilities stay <= 2^8.
   constexpr float kRescaleSlack = 8.f;
 
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][BN][KPK];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][BN][KPV];
+  // two K and two V tile buffers; the tile loop is unrolled by two so every LDS
+  // address is a per-lane base plus an immediate
+  __shared__ __attribute__((aligned(1024))) char k_lds0[TB];
+  __shared__ __attribute__((aligned(1024))) char k_lds1[TB];
+  __shared__ __attribute__((aligned(1024))) char v_lds0[TB];
+  __shared__ __attribute__((aligned(1024))) char v_lds1[TB];
 
   int b = 0, kvh = 0, tile = 0;
   if (!prefill_item(blockIdx.x, batch, Hkv, BM_TOK, max_tiles, cu_seqlens_q, b, kvh, tile))
@@ -149,7 +183,7 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_bf16_kernel(
   const int Lk = cu_seqlens_k[b + 1] - cu_seqlens_k[b];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
@@ -183,18 +217,22 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_bf16_kernel(
   const int n_kv = (k_end + BN - 1) / BN;
   const int first_masked_tile = (Lk - Lq + tok0) / BN;  // tiles before it need no mask
 
-  // ---- global -> register staging of one K/V tile.  Every load is unconditional:
-  // keys at or past Lk re-read the tile's last valid key (real data, never stale
-  // memory); their scores are masked and their probabilities are 0.
-  const int ld_row = tid / CPR;
-  const int ld_chunk = tid - ld_row * CPR;
-  u32x4_t kst[LIT], vst[LIT];
-  // block id of tile t (a vector load so it counts in order with the K/V loads;
-  // with BIG_BLOCK a 64-key tile lies in one block and every lane gets the same id)
+  // ---- global -> LDS loads of one K/V tile, straight into LDS (no register staging).
+  // Wavefront instruction i covers LDS rows (4i + wave) * RPL .. + RPL; lane l writes
+  // physical chunk l % CPR of row (4i + wave) * RPL + l / CPR and so loads that row's
+  // logical chunk (l % CPR) ^ swz(row).  Rows past the last valid key re-read it.
+  int ld_row[LIT], ld_chunk[LIT];
+#pragma unroll
+  for (int i = 0; i < LIT; ++i) {
+    ld_row[i] = (4 * i + wave) * RPL + lane / CPR;
+    ld_chunk[i] = (lane % CPR) ^ swz<D>(ld_row[i]);
+  }
+  // block id of tile t (with BIG_BLOCK a 64-key tile lies in one block and every lane
+  // gets the same id)
   auto tile_block = [&](int t) -> int {
     return table[min(t * BN + (lane & (BN - 1)), Lk - 1) >> bs_log2];
   };
-  auto fetch = [&](int t, int te) {
+  auto fetch = [&](int t, int te, char* kl, char* vl) {
     const int kv0 = t * BN;
     const int last = min(Lk - kv0, BN) - 1;
     if constexpr (BIG_BLOCK) {
@@ -203,53 +241,67 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_bf16_kernel(
       const char* kb = reinterpret_cast<const char*>(k_cache + first);
       const char* vb = reinterpret_cast<const char*>(v_cache + first);
 #pragma unroll
-      for (int it = 0; it < LIT; ++it) {
+      for (int i = 0; i < LIT; ++i) {
         const uint32_t off =
-            static_cast<uint32_t>(min(it * RPI + ld_row, last)) * row_bytes + ld_chunk * 16;
-        kst[it] = *reinterpret_cast<const u32x4_t*>(kb + off);
-        vst[it] = *reinterpret_cast<const u32x4_t*>(vb + off);
+            static_cast<uint32_t>(min(ld_row[i], last)) * row_bytes + ld_chunk[i] * 16;
+        const int lo = (4 * i + wave) * RPL * RB;
+        dma16(kb, off, lds_addr(kl + lo));
+        dma16(vb, off, lds_addr(vl + lo));
       }
     } else {
+      // every row's table entry first, so the loads go out together
+      int blk[LIT];
 #pragma unroll
-      for (int it = 0; it < LIT; ++it) {
-        const int key = kv0 + min(it * RPI + ld_row, last);
-        const int64_t off =
-            token_row(table[key >> bs_log2], key, bs_log2, Hkv, kvh, D) + ld_chunk * 8;
-        kst[it] = *reinterpret_cast<const u32x4_t*>(k_cache + off);
-        vst[it] = *reinterpret_cast<const u32x4_t*>(v_cache + off);
+      for (int i = 0; i < LIT; ++i) blk[i] = table[(kv0 + min(ld_row[i], last)) >> bs_log2];
+#pragma unroll
+      for (int i = 0; i < LIT; ++i) {
+        const int key = kv0 + min(ld_row[i], last);
+        const int64_t off = token_row(blk[i], key, bs_log2, Hkv, kvh, D) + ld_chunk[i] * 8;
+        const int lo = (4 * i + wave) * RPL * RB;
+        dma16_ptr(k_cache + off, lds_addr(kl + lo));
+        dma16_ptr(v_cache + off, lds_addr(vl + lo));
       }
     }
   };
-  auto stage = [&](int buf) {
+
+  // LDS read addresses (bytes within a tile): the K operand of k-step ks for this lane's
+  // key row l32 (+32 rows for the second 32-key block: immediate), and the V^T operand
+  // of head_dim tile dt for key row key_in (+16 rows per k-step, +8 for the second
+  // half: immediates)
+  int kaddr[KS];
 #pragma unroll
-    for (int it = 0; it < LIT; ++it) {
-      *reinterpret_cast<u32x4_t*>(&k_lds[buf][it * RPI + ld_row][ld_chunk * 8]) = kst[it];
-      *reinterpret_cast<u32x4_t*>(&v_lds[buf][it * RPI + ld_row][ld_chunk * 8]) = vst[it];
-    }
-  };
+  for (int ks = 0; ks < KS; ++ks) kaddr[ks] = l32 * RB + 16 * ((2 * ks + hi) ^ swz<D>(l32));
+  const int g16 = lane >> 4;
+  const int gl = lane & 15;
+  const int key_in = 4 * hi + (gl >> 2);
+  // (rows key_in and key_in + 8 of a k-step have different swizzles: two addresses)
+  int vaddr[DT], vaddr8[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    const int c = 4 * dt + 2 * (g16 & 1) + ((gl >> 1) & 1);
+    vaddr[dt] = key_in * RB + 16 * (c ^ swz<D>(key_in)) + 8 * (gl & 1);
+    vaddr8[dt] = (key_in + 8) * RB + 16 * (c ^ swz<D>(key_in + 8)) + 8 * (gl & 1);
+  }
 
   f32x16_t o[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
-  float m = -INFINITY;  // reference max of this row, scaled to the log2 domain
-  float l = 0.f;        // this lane's share of the row's sum of (bf16-rounded) probabilities
+  float m = -INFINITY;
+  float l = 0.f;
 
   int te_next = BIG_BLOCK ? tile_block(0) : 0;
-  fetch(0, te_next);
+  fetch(0, te_next, k_lds0, v_lds0);
   if (BIG_BLOCK && n_kv > 1) te_next = tile_block(1);
-  stage(0);
-  __syncthreads();
 
-  for (int t = 0; t < n_kv; ++t) {
-    const int buf = t & 1;
+  auto step = [&](int t, const char* kl, const char* vl, char* kn, char* vn) {
     const bool has_next = t + 1 < n_kv;
-    // the next tile's loads go out first and land while this tile is computed
+    // tile t has landed in LDS (every wave's share) and every wave is done with t-1
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    __syncthreads();
     if (has_next) {
-      fetch(t + 1, te_next);
-      // the entry after it reuses te_next's register: it is fetched only once the
-      // K/V loads have consumed the old value
+      fetch(t + 1, te_next, kn, vn);
       if (BIG_BLOCK) te_next = tile_block(min(t + 2, n_kv - 1));
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -263,7 +315,7 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_bf16_kernel(
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const bf16x8_t ka = __builtin_bit_cast(
-            bf16x8_t, *reinterpret_cast<const u32x4_t*>(&k_lds[buf][32 * sub + l32][ks * 16 + 8 * hi]));
+            bf16x8_t, *reinterpret_cast<const u32x4_t*>(kl + 32 * sub * RB + kaddr[ks]));
         s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[ks], s[sub], 0, 0, 0);
       }
     }
@@ -324,17 +376,14 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_bf16_kernel(
       }
 
     // ---- O^T += V^T P^T: A = V^T via transposing LDS reads, keys in the same order as P
-    const int g = lane >> 4;         // 16-lane group
-    const int gl = lane & 15;        // lane within the group
-    const int key_in = 4 * hi + (gl >> 2);
-    const int col_in = 16 * (g & 1) + 4 * (gl & 3);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const uint16_t* p0 = &v_lds[buf][16 * ks + key_in][32 * dt + col_in];
-        const i16x4_t lo4 = lds_read_tr16(p0);
-        const i16x4_t hi4 = lds_read_tr16(p0 + 8 * KPV);
+        const i16x4_t lo4 =
+            lds_read_tr16(reinterpret_cast<const uint16_t*>(vl + ks * 16 * RB + vaddr[dt]));
+        const i16x4_t hi4 =
+            lds_read_tr16(reinterpret_cast<const uint16_t*>(vl + ks * 16 * RB + vaddr8[dt]));
         const u32x2_t lo = __builtin_bit_cast(u32x2_t, lo4);
         const u32x2_t hi2 = __builtin_bit_cast(u32x2_t, hi4);
         const u32x4_t va = {lo[0], lo[1], hi2[0], hi2[1]};
@@ -342,9 +391,10 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_bf16_kernel(
                                                        o[dt], 0, 0, 0);
       }
     }
-
-    if (has_next) stage(buf ^ 1);
-    __syncthreads();
+  };
+  for (int t = 0; t < n_kv; t += 2) {
+    step(t, k_lds0, v_lds0, k_lds1, v_lds1);
+    if (t + 1 < n_kv) step(t + 1, k_lds1, v_lds1, k_lds0, v_lds0);
   }
 
   // ---- normalise and store: o[dt][r] is d = 32*dt + 8*(r/4) + 4*hi + r%4 of this row
