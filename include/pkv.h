@@ -13,9 +13,11 @@
  * by cumulative lengths; decode batches one token per sequence).
  *
  * Conventions for every call:
- *  - Every array pointer is a DEVICE pointer owned by the caller.  The library
- *    allocates no device memory, keeps no state between calls, never
- *    synchronises, and enqueues all its work on `stream`.  Calls are reentrant.
+ *  - Every array pointer of the data-plane calls (store, prefill, decode) is a
+ *    DEVICE pointer owned by the caller.  The library allocates no device memory,
+ *    keeps no state between calls, never synchronises, and enqueues all its work
+ *    on `stream`.  Calls are reentrant.  The block manager (pkv_bm_*) is host-only
+ *    and takes host arrays.
  *  - Element type: q, k, v, both caches and out share one type (pkv_dtype).
  *    Metadata arrays are int32.
  *  - Cache layout (one layer): k_cache and v_cache are each
@@ -50,7 +52,8 @@ typedef enum {
   PKV_ERR_INVALID = -1,     /* null pointer, negative size, inconsistent shapes */
   PKV_ERR_UNSUPPORTED = -2, /* head_dim, block_size or dtype outside what is built */
   PKV_ERR_WORKSPACE = -3,   /* decode workspace missing or too small */
-  PKV_ERR_HIP = -4          /* a kernel launch failed (hipGetLastError) */
+  PKV_ERR_HIP = -4,         /* a kernel launch failed (hipGetLastError) */
+  PKV_ERR_NO_BLOCKS = -5    /* block manager: too few free blocks (the scheduler preempts) */
 } pkv_status;
 
 typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
@@ -144,6 +147,85 @@ pkv_status pkv_paged_decode(const pkv_cache* cache, const void* q, void* out,
                             const int32_t* block_tables, int32_t block_table_stride,
                             float scale, void* workspace, size_t workspace_bytes,
                             int32_t num_workers, hipStream_t stream);
+
+/* ---- Block manager: the host control plane that hands out block ids.
+ * (“Nano-vLLM 引擎架构解析” section 3.2 "PagedAttention": a Block has an id, a
+ * reference count and its token ids; the manager keeps a deque of free blocks and
+ * hands out its head; blocks are reused by prefix hash and allocated on demand as a
+ * sequence grows.  “深入 Nano-vLLM 推理引擎”: "From Sequences to Blocks" (a sequence is
+ * cut into fixed-size blocks; two sequences never share a block's tokens), "Prefix
+ * Caching by hashing" (a hash -> block id map; a new sequence whose block hash is
+ * cached takes that block with one more reference), "Control plane vs. data plane"
+ * (the manager lives in host memory; a freed block is only marked free, its GPU
+ * contents are overwritten on reuse) and "Handling resource exhaustion" (when no
+ * block is free the scheduler preempts a sequence).)
+ *
+ * Host memory only: no device call is made.  A manager is not thread-safe; use one
+ * per control-plane thread.  Sequences are named by the ids pkv_bm_add_sequence
+ * returns.
+ *
+ * Prefix cache.  Only full blocks are cached.  Block j of a sequence (tokens
+ * j*block_size .. (j+1)*block_size - 1) has the hash h_j = FNV-1a-64 over the 8
+ * bytes of h_{j-1} (h_{-1} = the FNV offset basis) followed by the block's token
+ * ids (4 bytes each, little-endian), so equal hashes mean equal whole prefixes up
+ * to a 2^-64 collision; a hit also compares the block's own token ids.  When a
+ * sequence is allocated, its blocks are looked up from the first: every block up
+ * to the first miss is a hit and is reused (one more reference; a cached block that
+ * was freed but not yet handed out again is taken back off the free deque); every
+ * block from the first miss on, and the last partial block, gets a new block from
+ * the head of the free deque.  A new full block registers its hash at once (its
+ * K/V are written by the same step's pkv_store_kvcache, before any prefill reads
+ * them); a block handed out again loses its old registration, so a stale block is
+ * never a hit.  Freed blocks go to the tail of the free deque, the sequence's last
+ * block first. */
+typedef struct pkv_block_manager pkv_block_manager;
+
+/* A manager over block ids 0 .. num_blocks-1, all free; the free deque holds them in
+ * the order of free_order (a host array, a permutation of 0 .. num_blocks-1), or in
+ * id order when free_order is NULL.  num_blocks >= 1, block_size >= 1.  *out
+ * receives the handle (host memory). */
+pkv_status pkv_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
+                         pkv_block_manager** out);
+/* Frees the manager and everything it holds (NULL is a no-op). */
+void pkv_bm_destroy(pkv_block_manager* bm);
+/* Free blocks, or a negative pkv_status for a NULL manager. */
+int32_t pkv_bm_num_free(const pkv_block_manager* bm);
+/* Reference count of a block (0 = free), or a negative pkv_status. */
+int32_t pkv_bm_ref_count(const pkv_block_manager* bm, int32_t block);
+
+/* Registers a sequence with its first num_tokens token ids (a host array, copied;
+ * num_tokens >= 1); it holds no blocks yet.  *seq_out receives its id. */
+pkv_status pkv_bm_add_sequence(pkv_block_manager* bm, const int32_t* token_ids,
+                               int32_t num_tokens, int64_t* seq_out);
+/* Releases the sequence's blocks (if any) and forgets it. */
+pkv_status pkv_bm_remove_sequence(pkv_block_manager* bm, int64_t seq);
+/* 1 if pkv_bm_allocate would succeed now, 0 if not, negative pkv_status on error. */
+int32_t pkv_bm_can_allocate(const pkv_block_manager* bm, int64_t seq);
+/* Blocks for all of the sequence's tokens (prefill), prefix hits reused as above.
+ * PKV_ERR_NO_BLOCKS if too few are free (nothing changes); PKV_ERR_INVALID if the
+ * sequence already holds blocks. */
+pkv_status pkv_bm_allocate(pkv_block_manager* bm, int64_t seq);
+/* Leading tokens whose K/V were already cached at the last pkv_bm_allocate (a
+ * multiple of block_size; these need no prefill), or a negative pkv_status. */
+int32_t pkv_bm_num_cached_tokens(const pkv_block_manager* bm, int64_t seq);
+/* Tokens the sequence holds, or a negative pkv_status. */
+int32_t pkv_bm_num_tokens(const pkv_block_manager* bm, int64_t seq);
+/* 1 if pkv_bm_append_token would succeed now (a new block is needed only when the
+ * token starts one), 0 if not, negative pkv_status on error. */
+int32_t pkv_bm_can_append(const pkv_block_manager* bm, int64_t seq);
+/* Decode: appends one token id to an allocated sequence, taking a new block when
+ * the token starts one; a block that the token fills registers its hash.
+ * PKV_ERR_NO_BLOCKS if a block is needed and none is free (nothing changes). */
+pkv_status pkv_bm_append_token(pkv_block_manager* bm, int64_t seq, int32_t token_id);
+/* Preemption or completion: drops one reference from each of the sequence's blocks
+ * (a block at zero goes to the tail of the free deque, contents and hash kept); the
+ * sequence keeps its tokens and can be allocated again. */
+pkv_status pkv_bm_deallocate(pkv_block_manager* bm, int64_t seq);
+/* Copies the sequence's block table (up to capacity entries) to the host array
+ * out and returns its length, or a negative pkv_status.  out may be NULL with
+ * capacity 0 to ask for the length. */
+int32_t pkv_bm_block_table(const pkv_block_manager* bm, int64_t seq, int32_t* out,
+                           int32_t capacity);
 
 /* Kernel timing, off by default (tracing support for benchmarks).  While on,
  * every kernel the library launches is bracketed by two hipEvents recorded on

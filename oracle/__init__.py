@@ -19,11 +19,14 @@ Contents and what pins each part (tests/test_oracle.py):
 * ``block_manager`` - the pages' BlockManager (free deque, reference counts,
   prefix sharing) and the step planner.  Pinned by hand-worked allocation
   fixtures, reference-count and exhaustion invariants, and slot round trips.
+  ``PrefixCache`` models the prefix-cached manager keyed by whole token prefixes;
+  pinned by the hand-worked scenarios of tests/test_block_manager.py and the
+  reference-count / free-deque / registration invariants checked there.
 * ``step`` - a whole step (writes, then prefill and decode) on plain arrays.
 
 Everything is float64 unless a caller asks for float32; nothing is tuned.
 """
-from .block_manager import Block, BlockManager, cumulative_lengths, plan_step, slot_of
+from .block_manager import Block, BlockManager, PrefixCache, cumulative_lengths, plan_step, slot_of
 from .paged_attention import (as_float, bf16_bits_to_float, causal_attention, combine_partials,
                               decode_split_partials, gather_tokens, kv_head_of, paged_decode,
                               paged_prefill, store_kvcache)

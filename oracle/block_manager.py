@@ -29,7 +29,7 @@ from collections import deque
 
 import numpy as np
 
-__all__ = ["Block", "BlockManager", "slot_of", "cumulative_lengths", "plan_step"]
+__all__ = ["Block", "BlockManager", "PrefixCache", "slot_of", "cumulative_lengths", "plan_step"]
 
 
 class Block:
@@ -150,3 +150,123 @@ def plan_step(wl, table_pad: int = -1) -> dict:
         "decode_block_tables": padded(decode),
         "table_width": width,
     }
+
+
+class PrefixCache:
+    """Plain model of the prefix-cached block manager (test infrastructure only).
+
+    “深入 Nano-vLLM 推理引擎”, "Prefix Caching by hashing": the manager maps the hash of a
+    block to its id; a new sequence whose block is found takes it with one more
+    reference.  Here the map is keyed by the exact thing a chained block hash stands
+    for - the whole token prefix up to the end of the block - so the model needs no
+    hash function and has no collisions.  Readings (the pages are silent on them):
+
+    * only full blocks are cached; the last partial block is always new;
+    * lookups run from the first block and stop at the first miss (a prefix cache
+      reuses a cached prefix, not blocks after a gap);
+    * a new full block is registered at once; a block handed out again loses its
+      old registration, so stale contents are never a hit;
+    * a cached block that was freed (reference count 0) but not handed out again is
+      taken back off the free deque on a hit;
+    * a sequence's blocks are freed last block first, to the tail of the free deque;
+    * allocation and append are all-or-nothing when too few blocks are free.
+    """
+
+    def __init__(self, num_blocks: int, block_size: int, free_order=None):
+        order = range(num_blocks) if free_order is None else [int(b) for b in free_order]
+        self.bs = int(block_size)
+        self.free = deque(order)
+        self.ref = [0] * num_blocks
+        self.key_of = [None] * num_blocks   # the prefix a block is registered under
+        self.by_key = {}                    # prefix tuple -> block id
+        self.seqs = {}
+        self.next_id = 0
+
+    def add_sequence(self, tokens) -> int:
+        sid = self.next_id
+        self.next_id += 1
+        self.seqs[sid] = {"tokens": [int(t) for t in tokens], "table": [], "cached": 0}
+        return sid
+
+    def _plan(self, toks):
+        bs = self.bs
+        hits = []
+        for j in range(len(toks) // bs):
+            b = self.by_key.get(tuple(toks[:(j + 1) * bs]))
+            if b is None:
+                break
+            hits.append(b)
+        n_blocks = -(-len(toks) // bs)
+        takes = (n_blocks - len(hits)) + sum(1 for b in hits if self.ref[b] == 0)
+        return hits, takes
+
+    def can_allocate(self, sid) -> bool:
+        return self._plan(self.seqs[sid]["tokens"])[1] <= len(self.free)
+
+    def _take(self):
+        b = self.free.popleft()
+        if self.key_of[b] is not None:
+            if self.by_key.get(self.key_of[b]) == b:
+                del self.by_key[self.key_of[b]]
+            self.key_of[b] = None
+        self.ref[b] = 1
+        return b
+
+    def _register(self, b, key):
+        old = self.by_key.get(key)
+        if old is not None and old != b:
+            self.key_of[old] = None
+        self.by_key[key] = b
+        self.key_of[b] = key
+
+    def allocate(self, sid) -> bool:
+        s = self.seqs[sid]
+        if s["table"]:
+            raise ValueError("sequence already holds blocks")
+        toks, bs = s["tokens"], self.bs
+        hits, takes = self._plan(toks)
+        if takes > len(self.free):
+            return False
+        table = []
+        for b in hits:
+            if self.ref[b] == 0:
+                self.free.remove(b)
+                self.ref[b] = 1
+            else:
+                self.ref[b] += 1
+            table.append(b)
+        for j in range(len(hits), len(toks) // bs):
+            b = self._take()
+            self._register(b, tuple(toks[:(j + 1) * bs]))
+            table.append(b)
+        if len(toks) % bs:
+            table.append(self._take())
+        s["table"], s["cached"] = table, len(hits) * bs
+        return True
+
+    def can_append(self, sid) -> bool:
+        return len(self.seqs[sid]["tokens"]) % self.bs != 0 or len(self.free) > 0
+
+    def append_token(self, sid, token) -> bool:
+        s = self.seqs[sid]
+        n = len(s["tokens"])
+        if n % self.bs == 0:
+            if not self.free:
+                return False
+            s["table"].append(self._take())
+        s["tokens"].append(int(token))
+        if (n + 1) % self.bs == 0:
+            self._register(s["table"][-1], tuple(s["tokens"]))
+        return True
+
+    def deallocate(self, sid) -> None:
+        s = self.seqs[sid]
+        for b in reversed(s["table"]):
+            self.ref[b] -= 1
+            if self.ref[b] == 0:
+                self.free.append(b)
+        s["table"], s["cached"] = [], 0
+
+    def remove_sequence(self, sid) -> None:
+        self.deallocate(sid)
+        del self.seqs[sid]

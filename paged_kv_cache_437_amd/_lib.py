@@ -11,6 +11,7 @@ PKV_ERR_INVALID = -1
 PKV_ERR_UNSUPPORTED = -2
 PKV_ERR_WORKSPACE = -3
 PKV_ERR_HIP = -4
+PKV_ERR_NO_BLOCKS = -5
 PKV_F32 = 0
 PKV_BF16 = 1
 
@@ -18,6 +19,10 @@ EXPORTED = (
     "pkv_store_kvcache", "pkv_paged_prefill", "pkv_paged_decode_workspace_size",
     "pkv_paged_decode", "pkv_status_string", "pkv_last_error", "pkv_version",
     "pkv_timing_enable", "pkv_timing_collect",
+    "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_num_free", "pkv_bm_ref_count",
+    "pkv_bm_add_sequence", "pkv_bm_remove_sequence", "pkv_bm_can_allocate", "pkv_bm_allocate",
+    "pkv_bm_num_cached_tokens", "pkv_bm_num_tokens", "pkv_bm_can_append",
+    "pkv_bm_append_token", "pkv_bm_deallocate", "pkv_bm_block_table",
 )
 
 
@@ -81,6 +86,26 @@ def load() -> ctypes.CDLL:
     lib.pkv_timing_enable.restype = I
     lib.pkv_timing_collect.argtypes = [ctypes.POINTER(PkvKernelTiming), I]
     lib.pkv_timing_collect.restype = I
+    I64 = ctypes.c_int64
+    for name, args in (
+        ("pkv_bm_create", [I, I, P, ctypes.POINTER(P)]),
+        ("pkv_bm_num_free", [P]),
+        ("pkv_bm_ref_count", [P, I]),
+        ("pkv_bm_add_sequence", [P, P, I, ctypes.POINTER(I64)]),
+        ("pkv_bm_remove_sequence", [P, I64]),
+        ("pkv_bm_can_allocate", [P, I64]),
+        ("pkv_bm_allocate", [P, I64]),
+        ("pkv_bm_num_cached_tokens", [P, I64]),
+        ("pkv_bm_num_tokens", [P, I64]),
+        ("pkv_bm_can_append", [P, I64]),
+        ("pkv_bm_append_token", [P, I64, I]),
+        ("pkv_bm_deallocate", [P, I64]),
+        ("pkv_bm_block_table", [P, I64, P, I]),
+    ):
+        getattr(lib, name).argtypes = args
+        getattr(lib, name).restype = I
+    lib.pkv_bm_destroy.argtypes = [P]
+    lib.pkv_bm_destroy.restype = None
     _lib = lib
     return lib
 

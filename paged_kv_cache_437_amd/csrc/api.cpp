@@ -7,6 +7,7 @@
 #include <cstdio>
 
 #include "../../include/pkv.h"
+#include "errors.h"
 #include "launch.h"
 
 namespace {
@@ -25,6 +26,24 @@ pkv_status ok() {
   g_last_error[0] = '\0';
   return PKV_OK;
 }
+
+}  // namespace
+
+namespace pkv {
+
+pkv_status report_error(pkv_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+pkv_status report_ok() { return ok(); }
+
+}  // namespace pkv
+
+namespace {
 
 int log2_exact(int x) {
   int r = 0;
@@ -77,6 +96,7 @@ const char* pkv_status_string(pkv_status s) {
     case PKV_ERR_UNSUPPORTED: return "unsupported shape or dtype";
     case PKV_ERR_WORKSPACE: return "workspace missing or too small";
     case PKV_ERR_HIP: return "HIP launch error";
+    case PKV_ERR_NO_BLOCKS: return "KV block pool exhausted";
   }
   return "unknown status";
 }

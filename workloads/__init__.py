@@ -36,7 +36,7 @@ import numpy as np
 __all__ = [
     "SeqSpec", "Workload", "round_to_bf16_bits", "tiny_mixed", "decode_mha",
     "prefill_varlen", "prefill_prefix_cached", "decode_large", "by_name",
-    "CONFIG_NAMES", "block_bytes", "custom",
+    "CONFIG_NAMES", "block_bytes", "custom", "token_ids",
 ]
 
 
@@ -288,3 +288,25 @@ def by_name(name: str, seed: int = 0, **kw) -> Workload:
     return {"tiny_mixed": tiny_mixed, "decode_mha": decode_mha, "prefill_varlen": prefill_varlen,
             "prefill_prefix_cached": prefill_prefix_cached,
             "decode_large": decode_large}[name](seed=seed, **kw)
+
+
+def token_ids(wl: Workload, seed: int = 0, vocab: int = 151_936) -> list:
+    """Synthetic token ids for every sequence of a workload, ``context_len`` each:
+    sequences of one prefix group share their first ``prefix_len`` ids (drawn once
+    per group), every other id is drawn on its own, uniform on [0, vocab).  The
+    default vocabulary size is Qwen's, the model family the decode shape follows.
+    Draw order (``numpy.random.default_rng(seed)``): each group's prefix in group-id
+    order, then each sequence's own ids in sequence order."""
+    rng = np.random.default_rng(seed)
+    groups = {}
+    for s in wl.seqs:
+        if s.prefix_group >= 0 and s.prefix_group not in groups:
+            groups[s.prefix_group] = s.prefix_len
+    prefix_ids = {g: rng.integers(0, vocab, size=n, dtype=np.int64).astype(np.int32)
+                  for g, n in sorted(groups.items())}
+    out = []
+    for s in wl.seqs:
+        shared = prefix_ids[s.prefix_group] if s.prefix_group >= 0 else np.zeros(0, np.int32)
+        own = rng.integers(0, vocab, size=s.context_len - len(shared), dtype=np.int64)
+        out.append(np.concatenate([shared, own.astype(np.int32)]))
+    return out
