@@ -178,10 +178,48 @@ def cpu_baseline(wl, budget_s: float) -> dict:
                       f"batch, {secs:.1f} s)"}
 
 
-def prefill_leg(torch, pkv, workloads, DeviceStep, args) -> dict:
-    """Varlen causal prefill (16 prompts, lengths uniform on [128, 2048]) in TFLOP/s."""
+def graph_step(torch, pkv, step, wl, args) -> dict:
+    """Eager step time against the same step replayed from a HIP graph (one graph
+    launch instead of three kernel launches); the graph's static buffers are filled
+    once, then only the replays are timed."""
+    from paged_kv_cache_437_amd.graphs import DecodeStepGraph
+    n = len(step.plan.decode)
+    graph = DecodeStepGraph(step.k_cache, step.v_cache, wl.num_q_heads, n,
+                            step.decode_tables.shape[1], wl.scale)
+    graph.run(step.q_decode, step.k_new, step.v_new, step.slot_mapping, step.decode_tables,
+              step.context_lens)
+    for _ in range(args.warmup):
+        graph.graph.replay()
+    g_ms, _, _ = timed_steps(torch, pkv, graph.graph.replay, args.steps, kernel_events=False)
+    e_ms, _, _ = timed_steps(torch, pkv, step.run, args.steps, kernel_events=False)
+    del graph
+    return {"eager_ms_per_step": round(e_ms / args.steps, 5),
+            "graph_ms_per_step": round(g_ms / args.steps, 5)}
+
+
+def small_decode_graph(torch, pkv, workloads, DeviceStep, args) -> dict:
+    """The same comparison on a launch-bound decode step: 4 sequences of 150-400
+    tokens, 32 q / 32 kv heads, head_dim 128, block_size 256."""
+    from workloads import SeqSpec
+    ws = workloads.custom("decode_small_bf16", "bf16", 32, 32, 128, 256,
+                          [SeqSpec("decode", L, 1) for L in (200, 300, 150, 400)],
+                          seed=args.seed)
+    st = DeviceStep(ws, device="cuda", stale="nan")
+    for _ in range(args.warmup):
+        st.run()
+    torch.cuda.synchronize()
+    out = graph_step(torch, pkv, st, ws, args)
+    out["workload"] = "4 seqs, ctx 150-400, 32 q / 32 kv heads, head_dim 128, block_size 256"
+    del st
+    return out
+
+
+def prefill_leg(torch, pkv, workloads, DeviceStep, args, rotary: bool = False) -> dict:
+    """Varlen causal prefill (16 prompts, lengths uniform on [128, 2048]) in TFLOP/s;
+    with ``rotary`` the queries are rotated in the kernel's prologue (and K on write)."""
     wp = workloads.prefill_varlen(seed=args.seed)
-    ps = DeviceStep(wp, device="cuda", stale="nan")
+    table = pkv.rotary_table(4096, wp.head_dim) if rotary else None
+    ps = DeviceStep(wp, device="cuda", stale="nan", rotary=table)
     for _ in range(3):
         ps.run()
     torch.cuda.synchronize()
@@ -258,6 +296,7 @@ def main():
     d_bytes = decode_bytes(wl, plan)
     s_bytes = store_bytes(wl, n_new)
     value = (d_bytes + s_bytes) / (ms_per_step * 1e-3) / 1e9
+    graph_big = graph_step(torch, pkv, step, wl, args)
     decode_kernels = {k: v for k, v in kernels.items() if "decode" in k}
     dom_name = max(decode_kernels, key=lambda k: decode_kernels[k]["total_ms"])
     dom = decode_kernels[dom_name]
@@ -298,13 +337,32 @@ def main():
         },
         "kernels": {k: {"launches": v["launches"], "avg_ms": round(v["avg_ms"], 5)}
                     for k, v in kernels.items()},
+        "graph_step": {
+            "what": "decode step (KV write + decode) eager vs replayed from a HIP graph",
+            "this_workload": graph_big,
+            "launch_bound": small_decode_graph(torch, pkv, workloads, DeviceStep, args),
+        },
     }
+
+    # ---- the same decode step with rotary position embedding fused in (K rotated in
+    # the KV write, the queries in the decode kernel)
+    table = pkv.rotary_table(4096, wl.head_dim)
+    rstep = DeviceStep(wl, device="cuda", stale="nan", rotary=table)
+    for _ in range(args.warmup):
+        rstep.run()
+    r_ms, _, _ = timed_steps(torch, pkv, rstep.run, args.steps, kernel_events=False)
+    result["rotary"] = {"decode_ms_per_step": round(r_ms / args.steps, 5),
+                        "decode_value": round((d_bytes + s_bytes) / (r_ms / args.steps * 1e-3)
+                                              / 1e9, 2), "unit": "GB/s"}
+    del rstep
 
     # ---- varlen causal prefill, reported beside the decode line
     if not args.no_prefill:
         del step
         torch.cuda.empty_cache()
         result["prefill"] = prefill_leg(torch, pkv, workloads, DeviceStep, args)
+        result["rotary"]["prefill_tflops"] = prefill_leg(torch, pkv, workloads, DeviceStep, args,
+                                                         rotary=True)["achieved"]
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

@@ -84,6 +84,31 @@ pkv_status pkv_store_kvcache(const pkv_cache* cache, const void* k, const void* 
                              const int32_t* slot_mapping, int32_t num_tokens,
                              hipStream_t stream);
 
+/* Rotary position embedding (RoPE), fused into the KV write and into the attention
+ * calls' query prologue (“基于 nano-vLLM 学习大模型推理关键功能” §3.3 lists a rotary_embedding layer
+ * among the model's layers; the formula is RoFormer's (Su et al., 2021), with the
+ * half-split pairing: element i of a head row pairs with element i + head_dim/2).
+ * For a row x at position p, with c_i = cos(p * theta_i), s_i = sin(p * theta_i):
+ *   x'[i]              = x[i] * c_i - x[i + head_dim/2] * s_i
+ *   x'[i + head_dim/2] = x[i + head_dim/2] * c_i + x[i] * s_i,   i < head_dim/2,
+ * computed in fp32 and rounded once to the element type.  The table is the caller's:
+ *   cos_sin       device fp32 [max_position][head_dim]; row p holds c_0 .. c_{D/2-1}
+ *                 then s_0 .. s_{D/2-1} (theta_i = base^(-2i/head_dim) conventionally)
+ *   max_position  rows of the table (>= 1); a position outside [0, max_position) is a
+ *                 contract violation and reads the nearest row. */
+typedef struct {
+  const float* cos_sin;
+  int32_t max_position;
+} pkv_rotary;
+
+/* pkv_store_kvcache with K rotated at its token's position on the way in (V is copied
+ * bit for bit).
+ *   positions  [num_tokens] int32 device array: the token's position in its sequence */
+pkv_status pkv_store_kvcache_rotary(const pkv_cache* cache, const void* k, const void* v,
+                                    const int32_t* slot_mapping, const int32_t* positions,
+                                    int32_t num_tokens, const pkv_rotary* rotary,
+                                    hipStream_t stream);
+
 /* Varlen causal prefill (“深入 Nano-vLLM 推理引擎”, "Preparing for computation": sequences are
  * packed and addressed by cumulative lengths; "Prefix Caching": cached blocks
  * are read, not recomputed).  Sequence b owns query rows
@@ -108,6 +133,16 @@ pkv_status pkv_paged_prefill(const pkv_cache* cache, const void* q, void* out,
                              int32_t max_seqlen_q, int32_t max_seqlen_k,
                              const int32_t* block_tables, int32_t block_table_stride,
                              float scale, hipStream_t stream);
+
+/* pkv_paged_prefill with every query row rotated at its position (query i of a
+ * sequence sits at Lk - Lq + i) before the scores; the cached keys are expected to be
+ * rotated already (pkv_store_kvcache_rotary).  q itself is not modified. */
+pkv_status pkv_paged_prefill_rotary(const pkv_cache* cache, const void* q, void* out,
+                                    int32_t num_q_heads, int32_t batch,
+                                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                    int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                    const int32_t* block_tables, int32_t block_table_stride,
+                                    float scale, const pkv_rotary* rotary, hipStream_t stream);
 
 /* Bytes of device workspace pkv_paged_decode needs for this shape; num_workers as
  * in pkv_paged_decode.  0 for the fp32 path (it needs none) and for invalid
@@ -147,6 +182,16 @@ pkv_status pkv_paged_decode(const pkv_cache* cache, const void* q, void* out,
                             const int32_t* block_tables, int32_t block_table_stride,
                             float scale, void* workspace, size_t workspace_bytes,
                             int32_t num_workers, hipStream_t stream);
+
+/* pkv_paged_decode with each query rotated at its position, context_lens[b] - 1,
+ * before the scores (keys rotated already; q not modified). */
+pkv_status pkv_paged_decode_rotary(const pkv_cache* cache, const void* q, void* out,
+                                   int32_t num_q_heads, int32_t batch,
+                                   const int32_t* context_lens, int32_t max_context_len,
+                                   const int32_t* block_tables, int32_t block_table_stride,
+                                   float scale, void* workspace, size_t workspace_bytes,
+                                   int32_t num_workers, const pkv_rotary* rotary,
+                                   hipStream_t stream);
 
 /* ---- Block manager: the host control plane that hands out block ids.
  * (“Nano-vLLM 引擎架构解析” section 3.2 "PagedAttention": a Block has an id, a

@@ -23,6 +23,10 @@ Contents and what pins each part (tests/test_oracle.py):
   pinned by the hand-worked scenarios of tests/test_block_manager.py and the
   reference-count / free-deque / registration invariants checked there.
 * ``step`` - a whole step (writes, then prefill and decode) on plain arrays.
+* ``rotary`` - rotary position embedding (RoFormer's pair rotation, half-split
+  pairing) and a round-to-nearest-even bf16 rounding from its definition; pinned by
+  tests/test_rotary_oracle.py (identity at position 0, a hand-worked pair rotation,
+  pair norms, inverse and composition, relative-position scores, RNE ties).
 
 Everything is float64 unless a caller asks for float32; nothing is tuned.
 """

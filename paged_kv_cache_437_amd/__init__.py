@@ -29,7 +29,8 @@ from . import _lib
 from ._lib import PkvError
 
 __all__ = ["store_kvcache", "paged_prefill", "paged_decode", "paged_decode_workspace_size",
-           "PkvError", "version", "library_path", "timing_enable", "timing_collect"]
+           "rotary_table", "PkvError", "version", "library_path", "timing_enable",
+           "timing_collect"]
 
 _DTYPES = {torch.float32: _lib.PKV_F32, torch.bfloat16: _lib.PKV_BF16}
 
@@ -87,9 +88,32 @@ def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def rotary_table(max_position: int, head_dim: int, base: float = 10000.0,
+                 device="cuda") -> torch.Tensor:
+    """The rotary table the ``rotary=`` arguments take: fp32 [max_position, head_dim],
+    row p = cos(p * theta_i) for i < head_dim/2, then sin(p * theta_i), with
+    theta_i = base^(-2i/head_dim) (RoFormer's frequencies), computed in float64."""
+    i = torch.arange(head_dim // 2, dtype=torch.float64)
+    theta = base ** (-2.0 * i / head_dim)
+    ang = torch.arange(max_position, dtype=torch.float64)[:, None] * theta[None, :]
+    return torch.cat([ang.cos(), ang.sin()], dim=1).to(torch.float32).to(device).contiguous()
+
+
+def _rotary(rotary: torch.Tensor | None, like: torch.Tensor):
+    if rotary is None:
+        return None
+    if rotary.dtype != torch.float32 or rotary.dim() != 2 or rotary.shape[1] != like.shape[3]:
+        raise ValueError("rotary must be the fp32 [max_position, head_dim] table")
+    _dev(rotary, "rotary", torch.float32, like)
+    return _lib.PkvRotary(rotary.data_ptr(), rotary.shape[0])
+
+
 def store_kvcache(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor,
-                  v_cache: torch.Tensor, slot_mapping: torch.Tensor) -> None:
-    """k, v [N, Hkv, D] -> rows slot_mapping[t] of the caches (slot -1 skipped)."""
+                  v_cache: torch.Tensor, slot_mapping: torch.Tensor,
+                  positions: torch.Tensor | None = None,
+                  rotary: torch.Tensor | None = None) -> None:
+    """k, v [N, Hkv, D] -> rows slot_mapping[t] of the caches (slot -1 skipped).  With
+    ``rotary`` (rotary_table) K is rotated at ``positions`` [N] int32 on the way in."""
     lib = _lib.load()
     desc = _cache_desc(k_cache, v_cache)
     n = slot_mapping.numel()
@@ -97,14 +121,24 @@ def store_kvcache(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor,
         raise ValueError(f"k, v must be [{n}, Hkv, D] like the cache rows")
     args = (_dev(k, "k", k_cache.dtype, k_cache), _dev(v, "v", k_cache.dtype, k_cache),
             _dev(slot_mapping, "slot_mapping", torch.int32, k_cache))
-    _lib.check(lib.pkv_store_kvcache(ctypes.byref(desc), *args, n, _stream(k_cache.device)))
+    rot = _rotary(rotary, k_cache)
+    if rot is None:
+        _lib.check(lib.pkv_store_kvcache(ctypes.byref(desc), *args, n, _stream(k_cache.device)))
+        return
+    if positions is None or positions.numel() != n:
+        raise ValueError("rotary needs positions [N] int32")
+    _lib.check(lib.pkv_store_kvcache_rotary(ctypes.byref(desc), *args,
+                                            _dev(positions, "positions", torch.int32, k_cache),
+                                            n, ctypes.byref(rot), _stream(k_cache.device)))
 
 
 def paged_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                   cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor,
                   block_tables: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int,
-                  scale: float, out: torch.Tensor | None = None) -> torch.Tensor:
-    """q [total_q, Hq, D] -> out [total_q, Hq, D]; sequences packed by cu_seqlens."""
+                  scale: float, out: torch.Tensor | None = None,
+                  rotary: torch.Tensor | None = None) -> torch.Tensor:
+    """q [total_q, Hq, D] -> out [total_q, Hq, D]; sequences packed by cu_seqlens.  With
+    ``rotary`` every query row is rotated at its position first."""
     lib = _lib.load()
     desc = _cache_desc(k_cache, v_cache)
     if q.dim() != 3 or q.shape[2] != k_cache.shape[3]:
@@ -123,7 +157,12 @@ def paged_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
             _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32, k_cache), int(max_seqlen_q),
             int(max_seqlen_k), _dev(block_tables, "block_tables", torch.int32, k_cache),
             block_tables.shape[1], float(scale))
-    _lib.check(lib.pkv_paged_prefill(ctypes.byref(desc), *args, _stream(k_cache.device)))
+    rot = _rotary(rotary, k_cache)
+    if rot is None:
+        _lib.check(lib.pkv_paged_prefill(ctypes.byref(desc), *args, _stream(k_cache.device)))
+    else:
+        _lib.check(lib.pkv_paged_prefill_rotary(ctypes.byref(desc), *args, ctypes.byref(rot),
+                                                _stream(k_cache.device)))
     return out
 
 
@@ -137,8 +176,10 @@ def paged_decode_workspace_size(k_cache: torch.Tensor, v_cache: torch.Tensor, nu
 def paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                  block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
                  scale: float, num_workers: int = 0, out: torch.Tensor | None = None,
-                 workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """q [B, Hq, D] -> out [B, Hq, D]; one query per sequence over its context."""
+                 workspace: torch.Tensor | None = None,
+                 rotary: torch.Tensor | None = None) -> torch.Tensor:
+    """q [B, Hq, D] -> out [B, Hq, D]; one query per sequence over its context.  With
+    ``rotary`` each query is rotated at position context_len - 1 first."""
     lib = _lib.load()
     desc = _cache_desc(k_cache, v_cache)
     if q.dim() != 3 or q.shape[2] != k_cache.shape[3]:
@@ -160,5 +201,10 @@ def paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
             q.shape[1], batch, _dev(context_lens, "context_lens", torch.int32, k_cache),
             int(max_context_len), _dev(block_tables, "block_tables", torch.int32, k_cache),
             block_tables.shape[1], float(scale), ws_ptr, ws_bytes, int(num_workers))
-    _lib.check(lib.pkv_paged_decode(ctypes.byref(desc), *args, _stream(k_cache.device)))
+    rot = _rotary(rotary, k_cache)
+    if rot is None:
+        _lib.check(lib.pkv_paged_decode(ctypes.byref(desc), *args, _stream(k_cache.device)))
+    else:
+        _lib.check(lib.pkv_paged_decode_rotary(ctypes.byref(desc), *args, ctypes.byref(rot),
+                                               _stream(k_cache.device)))
     return out

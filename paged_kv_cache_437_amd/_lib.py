@@ -18,6 +18,7 @@ PKV_BF16 = 1
 EXPORTED = (
     "pkv_store_kvcache", "pkv_paged_prefill", "pkv_paged_decode_workspace_size",
     "pkv_paged_decode", "pkv_status_string", "pkv_last_error", "pkv_version",
+    "pkv_store_kvcache_rotary", "pkv_paged_prefill_rotary", "pkv_paged_decode_rotary",
     "pkv_timing_enable", "pkv_timing_collect",
     "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_num_free", "pkv_bm_ref_count",
     "pkv_bm_add_sequence", "pkv_bm_remove_sequence", "pkv_bm_can_allocate", "pkv_bm_allocate",
@@ -36,6 +37,10 @@ class PkvCache(ctypes.Structure):
         ("head_dim", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
     ]
+
+
+class PkvRotary(ctypes.Structure):
+    _fields_ = [("cos_sin", ctypes.c_void_p), ("max_position", ctypes.c_int32)]
 
 
 class PkvKernelTiming(ctypes.Structure):
@@ -76,6 +81,15 @@ def load() -> ctypes.CDLL:
     lib.pkv_paged_decode.argtypes = [cache_p, P, P, I, I, P, I, P, I, ctypes.c_float, P,
                                      ctypes.c_size_t, I, P]
     lib.pkv_paged_decode.restype = I
+    rot_p = ctypes.POINTER(PkvRotary)
+    lib.pkv_store_kvcache_rotary.argtypes = [cache_p, P, P, P, P, I, rot_p, P]
+    lib.pkv_store_kvcache_rotary.restype = I
+    lib.pkv_paged_prefill_rotary.argtypes = [cache_p, P, P, I, I, P, P, I, I, P, I,
+                                             ctypes.c_float, rot_p, P]
+    lib.pkv_paged_prefill_rotary.restype = I
+    lib.pkv_paged_decode_rotary.argtypes = [cache_p, P, P, I, I, P, I, P, I, ctypes.c_float, P,
+                                            ctypes.c_size_t, I, rot_p, P]
+    lib.pkv_paged_decode_rotary.restype = I
     lib.pkv_status_string.argtypes = [I]
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.pkv_last_error.argtypes = []

@@ -75,6 +75,15 @@ pkv_status check_heads(const pkv_cache* c, int32_t num_q_heads) {
   return PKV_OK;
 }
 
+pkv_status check_rotary(const pkv_cache* cache, const pkv_rotary* rot) {
+  if (rot == nullptr) return fail(PKV_ERR_INVALID, "rotary descriptor is NULL");
+  if (rot->cos_sin == nullptr) return fail(PKV_ERR_INVALID, "rotary cos_sin table is NULL");
+  if (rot->max_position < 1)
+    return fail(PKV_ERR_INVALID, "rotary max_position %d < 1", rot->max_position);
+  (void)cache;
+  return PKV_OK;
+}
+
 pkv_status launched(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
   return ok();
@@ -105,6 +114,24 @@ const char* pkv_last_error(void) { return g_last_error; }
 
 int32_t pkv_version(void) { return 200; }
 
+pkv_status pkv_store_kvcache_rotary(const pkv_cache* cache, const void* k, const void* v,
+                                    const int32_t* slot_mapping, const int32_t* positions,
+                                    int32_t num_tokens, const pkv_rotary* rotary,
+                                    hipStream_t stream) {
+  pkv_status st = check_cache(cache);
+  if (st != PKV_OK) return st;
+  if ((st = check_rotary(cache, rotary)) != PKV_OK) return st;
+  if (num_tokens < 0) return fail(PKV_ERR_INVALID, "num_tokens %d < 0", num_tokens);
+  if (num_tokens == 0) return ok();
+  if (k == nullptr || v == nullptr || slot_mapping == nullptr || positions == nullptr)
+    return fail(PKV_ERR_INVALID, "k, v, slot_mapping or positions is NULL");
+  return launched(pkv::launch_store_kvcache_rotary(
+                      cache->dtype == PKV_BF16, cache->head_dim, cache->k_cache, cache->v_cache,
+                      k, v, slot_mapping, positions, num_tokens, cache->num_kv_heads,
+                      rotary->cos_sin, rotary->max_position, stream),
+                  "store_kvcache_rotary");
+}
+
 pkv_status pkv_store_kvcache(const pkv_cache* cache, const void* k, const void* v,
                              const int32_t* slot_mapping, int32_t num_tokens,
                              hipStream_t stream) {
@@ -121,12 +148,13 @@ pkv_status pkv_store_kvcache(const pkv_cache* cache, const void* k, const void* 
                   "store_kvcache");
 }
 
-pkv_status pkv_paged_prefill(const pkv_cache* cache, const void* q, void* out,
-                             int32_t num_q_heads, int32_t batch,
-                             const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
-                             int32_t max_seqlen_q, int32_t max_seqlen_k,
-                             const int32_t* block_tables, int32_t block_table_stride,
-                             float scale, hipStream_t stream) {
+namespace {
+
+pkv_status prefill_impl(const pkv_cache* cache, const void* q, void* out, int32_t num_q_heads,
+                        int32_t batch, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                        int32_t max_seqlen_q, int32_t max_seqlen_k, const int32_t* block_tables,
+                        int32_t block_table_stride, float scale, const pkv_rotary* rot,
+                        hipStream_t stream) {
   pkv_status st = check_cache(cache);
   if (st != PKV_OK) return st;
   if ((st = check_heads(cache, num_q_heads)) != PKV_OK) return st;
@@ -147,18 +175,47 @@ pkv_status pkv_paged_prefill(const pkv_cache* cache, const void* q, void* out,
   if (!(scale > 0.f) || !std::isfinite(scale))
     return fail(PKV_ERR_INVALID, "scale %g must be finite and positive", scale);
   const int bs_log2 = log2_exact(cache->block_size);
+  const float* cs = rot != nullptr ? rot->cos_sin : nullptr;
+  const int max_pos = rot != nullptr ? rot->max_position : 0;
   if (cache->dtype == PKV_BF16)
     return launched(pkv::launch_paged_prefill_bf16(
                         cache->head_dim, q, out, cache->k_cache, cache->v_cache, num_q_heads,
                         cache->num_kv_heads, bs_log2, batch, max_seqlen_q, cu_seqlens_q,
-                        cu_seqlens_k, block_tables, block_table_stride, scale, stream),
+                        cu_seqlens_k, block_tables, block_table_stride, scale, cs, max_pos,
+                        stream),
                     "paged_prefill");
   return launched(pkv::launch_attention_generic(
                       false, cache->head_dim, q, out, cache->k_cache, cache->v_cache,
                       num_q_heads, cache->num_kv_heads, bs_log2, batch, max_seqlen_q,
                       cu_seqlens_q, cu_seqlens_k, nullptr, block_tables, block_table_stride,
-                      scale, stream),
+                      scale, cs, max_pos, stream),
                   "paged_prefill");
+}
+
+}  // namespace
+
+pkv_status pkv_paged_prefill(const pkv_cache* cache, const void* q, void* out,
+                             int32_t num_q_heads, int32_t batch,
+                             const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                             int32_t max_seqlen_q, int32_t max_seqlen_k,
+                             const int32_t* block_tables, int32_t block_table_stride,
+                             float scale, hipStream_t stream) {
+  return prefill_impl(cache, q, out, num_q_heads, batch, cu_seqlens_q, cu_seqlens_k,
+                      max_seqlen_q, max_seqlen_k, block_tables, block_table_stride, scale,
+                      nullptr, stream);
+}
+
+pkv_status pkv_paged_prefill_rotary(const pkv_cache* cache, const void* q, void* out,
+                                    int32_t num_q_heads, int32_t batch,
+                                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                    int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                    const int32_t* block_tables, int32_t block_table_stride,
+                                    float scale, const pkv_rotary* rotary, hipStream_t stream) {
+  const pkv_status st = check_rotary(cache, rotary);
+  if (st != PKV_OK) return st;
+  return prefill_impl(cache, q, out, num_q_heads, batch, cu_seqlens_q, cu_seqlens_k,
+                      max_seqlen_q, max_seqlen_k, block_tables, block_table_stride, scale,
+                      rotary, stream);
 }
 
 size_t pkv_paged_decode_workspace_size(const pkv_cache* cache, int32_t num_q_heads,
@@ -174,12 +231,13 @@ size_t pkv_paged_decode_workspace_size(const pkv_cache* cache, int32_t num_q_hea
                                           batch, num_workers);
 }
 
-pkv_status pkv_paged_decode(const pkv_cache* cache, const void* q, void* out,
-                            int32_t num_q_heads, int32_t batch,
-                            const int32_t* context_lens, int32_t max_context_len,
-                            const int32_t* block_tables, int32_t block_table_stride,
-                            float scale, void* workspace, size_t workspace_bytes,
-                            int32_t num_workers, hipStream_t stream) {
+namespace {
+
+pkv_status decode_impl(const pkv_cache* cache, const void* q, void* out, int32_t num_q_heads,
+                       int32_t batch, const int32_t* context_lens, int32_t max_context_len,
+                       const int32_t* block_tables, int32_t block_table_stride, float scale,
+                       void* workspace, size_t workspace_bytes, int32_t num_workers,
+                       const pkv_rotary* rot, hipStream_t stream) {
   pkv_status st = check_cache(cache);
   if (st != PKV_OK) return st;
   if ((st = check_heads(cache, num_q_heads)) != PKV_OK) return st;
@@ -204,17 +262,47 @@ pkv_status pkv_paged_decode(const pkv_cache* cache, const void* q, void* out,
   if (ws > 0 && (workspace == nullptr || workspace_bytes < ws))
     return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, ws);
   const int bs_log2 = log2_exact(cache->block_size);
+  const float* cs = rot != nullptr ? rot->cos_sin : nullptr;
+  const int max_pos = rot != nullptr ? rot->max_position : 0;
   if (cache->dtype == PKV_BF16)
     return launched(pkv::launch_paged_decode_bf16(
                         cache->head_dim, q, out, cache->k_cache, cache->v_cache, num_q_heads,
                         cache->num_kv_heads, bs_log2, batch, context_lens, block_tables,
-                        block_table_stride, scale, num_workers, workspace, stream),
+                        block_table_stride, scale, num_workers, workspace, cs, max_pos, stream),
                     "paged_decode");
   return launched(pkv::launch_attention_generic(
                       false, cache->head_dim, q, out, cache->k_cache, cache->v_cache,
                       num_q_heads, cache->num_kv_heads, bs_log2, batch, 1, nullptr, nullptr,
-                      context_lens, block_tables, block_table_stride, scale, stream),
+                      context_lens, block_tables, block_table_stride, scale, cs, max_pos,
+                      stream),
                   "paged_decode");
+}
+
+}  // namespace
+
+pkv_status pkv_paged_decode(const pkv_cache* cache, const void* q, void* out,
+                            int32_t num_q_heads, int32_t batch,
+                            const int32_t* context_lens, int32_t max_context_len,
+                            const int32_t* block_tables, int32_t block_table_stride,
+                            float scale, void* workspace, size_t workspace_bytes,
+                            int32_t num_workers, hipStream_t stream) {
+  return decode_impl(cache, q, out, num_q_heads, batch, context_lens, max_context_len,
+                     block_tables, block_table_stride, scale, workspace, workspace_bytes,
+                     num_workers, nullptr, stream);
+}
+
+pkv_status pkv_paged_decode_rotary(const pkv_cache* cache, const void* q, void* out,
+                                   int32_t num_q_heads, int32_t batch,
+                                   const int32_t* context_lens, int32_t max_context_len,
+                                   const int32_t* block_tables, int32_t block_table_stride,
+                                   float scale, void* workspace, size_t workspace_bytes,
+                                   int32_t num_workers, const pkv_rotary* rotary,
+                                   hipStream_t stream) {
+  const pkv_status st = check_rotary(cache, rotary);
+  if (st != PKV_OK) return st;
+  return decode_impl(cache, q, out, num_q_heads, batch, context_lens, max_context_len,
+                     block_tables, block_table_stride, scale, workspace, workspace_bytes,
+                     num_workers, rotary, stream);
 }
 
 }  // extern "C"

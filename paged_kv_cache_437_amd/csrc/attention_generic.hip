@@ -23,7 +23,7 @@ __global__ __launch_bounds__(256) void attention_generic_kernel(
     const T* __restrict__ v_cache, int Hq, int Hkv, int bs_log2,
     const int32_t* __restrict__ cu_seqlens_q, const int32_t* __restrict__ cu_seqlens_k,
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ block_tables,
-    int table_stride, float scale_log2) {
+    int table_stride, float scale_log2, const float* __restrict__ cos_sin, int max_position) {
   constexpr int E = D / 64;  // head_dim elements per lane in the P.V phase
   __shared__ float q_lds[4][D];
 
@@ -54,6 +54,25 @@ __global__ __launch_bounds__(256) void attention_generic_kernel(
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (cos_sin != nullptr) {
+    // rotary position embedding of the query at its position (half-split pairs: lane j
+    // rotates elements j and j + D/2), in fp32
+    const float* cs = cos_sin + static_cast<int64_t>(min(max(last_key, 0), max_position - 1)) * D;
+    float x = 0.f, y = 0.f;
+    if (lane < D / 2) {
+      x = q_lds[wave][lane];
+      y = q_lds[wave][lane + D / 2];
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (lane < D / 2) {
+      const float c = cs[lane], sn = cs[D / 2 + lane];
+      q_lds[wave][lane] = x * c - y * sn;
+      q_lds[wave][lane + D / 2] = y * c + x * sn;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
 
   float m = -INFINITY;  // running max of the log2-domain scores
   float l = 0.f;        // running sum of exp2(score - m)
@@ -101,13 +120,14 @@ template <typename T, int D>
 static void launch_one(const void* q, void* out, const void* kc, const void* vc, int Hq, int Hkv,
                        int bs_log2, int batch, int max_q_rows, const int32_t* cu_q,
                        const int32_t* cu_k, const int32_t* ctx, const int32_t* tables,
-                       int stride, float scale_log2, hipStream_t stream) {
+                       int stride, float scale_log2, const float* cos_sin, int max_position,
+                       hipStream_t stream) {
   dim3 grid((max_q_rows + 3) / 4, batch, Hq);
   timing_begin(ctx != nullptr ? "attention_generic_decode" : "attention_generic_prefill", stream);
   hipLaunchKernelGGL((attention_generic_kernel<T, D>), grid, dim3(256), 0, stream,
                      static_cast<const T*>(q), static_cast<T*>(out), static_cast<const T*>(kc),
                      static_cast<const T*>(vc), Hq, Hkv, bs_log2, cu_q, cu_k, ctx, tables, stride,
-                     scale_log2);
+                     scale_log2, cos_sin, max_position);
   timing_end(stream);
 }
 
@@ -116,13 +136,14 @@ hipError_t launch_attention_generic(bool bf16, int head_dim, const void* q, void
                                     int num_kv_heads, int bs_log2, int batch, int max_q_rows,
                                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                                     const int32_t* context_lens, const int32_t* block_tables,
-                                    int table_stride, float scale, hipStream_t stream) {
+                                    int table_stride, float scale, const float* cos_sin,
+                                    int max_position, hipStream_t stream) {
   if (batch == 0 || max_q_rows == 0) return hipSuccess;
   const float scale_log2 = scale * kLog2e;
 #define PKV_GENERIC(T, D)                                                                      \
   launch_one<T, D>(q, out, k_cache, v_cache, num_q_heads, num_kv_heads, bs_log2, batch,        \
                    max_q_rows, cu_seqlens_q, cu_seqlens_k, context_lens, block_tables,         \
-                   table_stride, scale_log2, stream)
+                   table_stride, scale_log2, cos_sin, max_position, stream)
   if (bf16) {
     if (head_dim == 64) PKV_GENERIC(uint16_t, 64); else PKV_GENERIC(uint16_t, 128);
   } else {

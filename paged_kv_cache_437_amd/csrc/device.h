@@ -28,6 +28,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Rotary position embedding on 8 bf16 elements x (first half of a head row) and
+// their partners y (the same elements + head_dim/2), both as 16-byte words, with
+// the cosines c and sines s of those elements: x' = x c - y s, y' = y c + x s in fp32,
+// each rounded once to bf16 (round to nearest even).
+__device__ __forceinline__ void rope8_bf16(uint32_t (&x)[4], uint32_t (&y)[4], const float* c,
+                                           const float* s) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float x0 = bf16_lo(x[w]), x1 = bf16_hi(x[w]);
+    const float y0 = bf16_lo(y[w]), y1 = bf16_hi(y[w]);
+    const float c0 = c[2 * w], c1 = c[2 * w + 1], s0 = s[2 * w], s1 = s[2 * w + 1];
+    x[w] = pack_bf16x2(x0 * c0 - y0 * s0, x1 * c1 - y1 * s1);
+    y[w] = pack_bf16x2(y0 * c0 + x0 * s0, y1 * c1 + x1 * s1);
+  }
+}
+
 // Element <-> float for the two storage types.
 template <typename T> struct Elem;
 template <> struct Elem<float> {

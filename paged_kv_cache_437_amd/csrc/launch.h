@@ -13,6 +13,15 @@ hipError_t launch_store_kvcache(void* k_cache, void* v_cache, const void* k, con
                                 const int32_t* slot_mapping, int32_t num_tokens,
                                 int32_t row_bytes, hipStream_t stream);
 
+// The same with K rotated at positions[t] on the way in (rotary table cos_sin,
+// [max_position][head_dim] fp32); V copied.
+hipError_t launch_store_kvcache_rotary(bool bf16, int head_dim, void* k_cache, void* v_cache,
+                                       const void* k, const void* v,
+                                       const int32_t* slot_mapping, const int32_t* positions,
+                                       int32_t num_tokens, int num_kv_heads,
+                                       const float* cos_sin, int max_position,
+                                       hipStream_t stream);
+
 // Generic attention: one wavefront per (query row, q head), vector ALU only.  Serves
 // fp32 prefill and decode.  Decode when `context_lens` is non-null (one query per
 // sequence), otherwise packed prefill over cu_seqlens_q / cu_seqlens_k.
@@ -21,8 +30,10 @@ hipError_t launch_attention_generic(bool bf16, int head_dim, const void* q, void
                                     int num_kv_heads, int bs_log2, int batch, int max_q_rows,
                                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                                     const int32_t* context_lens, const int32_t* block_tables,
-                                    int table_stride, float scale, hipStream_t stream);
+                                    int table_stride, float scale, const float* cos_sin,
+                                    int max_position, hipStream_t stream);
 
+// With cos_sin non-null, each query is rotated at position context_len - 1.
 // bf16 paged decode: the streaming kernel over `num_workers` wavefront workers (0 =
 // as many as the device holds resident) and the combine kernel for streams cut
 // between workers.  The workspace holds, 256-byte aligned one after the other:
@@ -35,14 +46,16 @@ hipError_t launch_paged_decode_bf16(int head_dim, const void* q, void* out, cons
                                     const void* v_cache, int num_q_heads, int num_kv_heads,
                                     int bs_log2, int batch, const int32_t* context_lens,
                                     const int32_t* block_tables, int table_stride, float scale,
-                                    int num_workers, void* workspace, hipStream_t stream);
+                                    int num_workers, void* workspace, const float* cos_sin,
+                                    int max_position, hipStream_t stream);
 
-// bf16 varlen causal prefill on MFMA (one launch).
+// bf16 varlen causal prefill on MFMA (one launch).  With cos_sin non-null, every query
+// row is rotated at its position (rotary table [max_position][head_dim] fp32).
 hipError_t launch_paged_prefill_bf16(int head_dim, const void* q, void* out, const void* k_cache,
                                      const void* v_cache, int num_q_heads, int num_kv_heads,
                                      int bs_log2, int batch, int max_seqlen_q,
                                      const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                                      const int32_t* block_tables, int table_stride, float scale,
-                                     hipStream_t stream);
+                                     const float* cos_sin, int max_position, hipStream_t stream);
 
 }  // namespace pkv

@@ -179,7 +179,7 @@ __device__ __forceinline__ float sub_sum(float x) {
 
 // (at least two waves per SIMD: the eight-head groups would otherwise take a few
 // registers past 256 and run one wave per SIMD)
-template <int D, int GP, int MH, bool ONE_BLOCK>
+template <int D, int GP, int MH, bool ONE_BLOCK, bool ROT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void
 paged_decode_bf16_kernel(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
@@ -187,7 +187,8 @@ paged_decode_bf16_kernel(
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ block_tables,
     int table_stride, int batch, int Hq, int Hkv, int G, int n_hg, int bs_log2,
     float scale_log2, int num_workers, int64_t* __restrict__ ws_prefix,
-    float2* __restrict__ ws_ml, float* __restrict__ ws_o) {
+    float2* __restrict__ ws_ml, float* __restrict__ ws_o, const float* __restrict__ cos_sin,
+    int max_position) {
   static_assert(D == 64 || D == 128, "head_dim");
   static_assert(GP == 1 || GP == 2 || GP == 4 || GP == 8, "q heads per kv head in a stream");
   constexpr int DCH = D / 8;         // 16-byte pieces per head row
@@ -329,6 +330,30 @@ paged_decode_bf16_kernel(
 #pragma unroll
       for (int g = 0; g < GP; ++g)
         qv[g] = *reinterpret_cast<const u32x4_t*>(qb + min(g, nh - 1) * D);
+    }
+    if constexpr (ROT) {
+      // rotary position embedding of the query at the context's last position: this
+      // lane's 8 elements pair with the lane DCH/2 away (the other half of the head
+      // row); x' = x c - y s in the first half, y' = y c + x s in the second, in fp32
+      const int pos = min(max(x.L - 1, 0), max_position - 1);
+      const float* cs = cos_sin + static_cast<int64_t>(pos) * D + (piece & (DCH / 2 - 1)) * 8;
+      const float sgn = piece < DCH / 2 ? -1.f : 1.f;
+      float c[8], sn[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        c[e] = cs[e];
+        sn[e] = sgn * cs[D / 2 + e];
+      }
+#pragma unroll
+      for (int g = 0; g < GP; ++g)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t own = qv[g][w];
+          const uint32_t other =
+              static_cast<uint32_t>(__shfl_xor(static_cast<int>(own), DCH / 2, 64));
+          qv[g][w] = pack_bf16x2(bf16_lo(own) * c[2 * w] + bf16_lo(other) * sn[2 * w],
+                                 bf16_hi(own) * c[2 * w + 1] + bf16_hi(other) * sn[2 * w + 1]);
+        }
     }
   };
   auto issue = [&](const Cursor& x, int te, Buf& buf, bool live) {
@@ -546,7 +571,8 @@ int auto_workers() {
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu, reinterpret_cast<const void*>(&paged_decode_bf16_kernel<D, GP, MH, ONE_BLOCK>),
+          &per_cu,
+          reinterpret_cast<const void*>(&paged_decode_bf16_kernel<D, GP, MH, ONE_BLOCK, false>),
           256, 0) != hipSuccess ||
       cus <= 0 || per_cu <= 0) {
     cus = 256;
@@ -567,7 +593,7 @@ hipError_t launch_decode(const void* q, void* out, const void* k_cache, const vo
                          int num_q_heads, int num_kv_heads, int bs_log2, int batch,
                          const int32_t* context_lens, const int32_t* block_tables,
                          int table_stride, float scale, int num_workers, void* workspace,
-                         hipStream_t stream) {
+                         const float* cos_sin, int max_position, hipStream_t stream) {
   const int G = num_q_heads / num_kv_heads;
   const int n_hg = (G + GP - 1) / GP;
   const int S = (num_kv_heads / MH) * n_hg;
@@ -576,12 +602,14 @@ hipError_t launch_decode(const void* q, void* out, const void* k_cache, const vo
   const DecodeWorkspace ws = carve_decode_workspace(workspace, batch, W, MH * GP);
   const float scale_log2 = scale * kLog2e;
   timing_begin("paged_decode", stream);
-  hipLaunchKernelGGL((paged_decode_bf16_kernel<D, GP, MH, ONE_BLOCK>), dim3((W + 3) / 4),
-                     dim3(256), 0, stream, static_cast<const uint16_t*>(q),
-                     static_cast<uint16_t*>(out), static_cast<const uint16_t*>(k_cache),
-                     static_cast<const uint16_t*>(v_cache), context_lens, block_tables,
-                     table_stride, batch, num_q_heads, num_kv_heads, G, n_hg, bs_log2,
-                     scale_log2, W, ws.prefix, ws.ml, ws.o);
+  auto kernel = cos_sin != nullptr ? paged_decode_bf16_kernel<D, GP, MH, ONE_BLOCK, true>
+                                   : paged_decode_bf16_kernel<D, GP, MH, ONE_BLOCK, false>;
+  hipLaunchKernelGGL(kernel, dim3((W + 3) / 4), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(q), static_cast<uint16_t*>(out),
+                     static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache),
+                     context_lens, block_tables, table_stride, batch, num_q_heads, num_kv_heads, G,
+                     n_hg, bs_log2, scale_log2, W, ws.prefix, ws.ml, ws.o, cos_sin,
+                     max_position);
   timing_end(stream);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -594,15 +622,17 @@ hipError_t launch_decode_bs(const void* q, void* out, const void* k_cache, const
                             int num_q_heads, int num_kv_heads, int bs_log2, int batch,
                             const int32_t* context_lens, const int32_t* block_tables,
                             int table_stride, float scale, int num_workers, void* workspace,
-                            hipStream_t stream) {
+                            const float* cos_sin, int max_position, hipStream_t stream) {
   // ONE_BLOCK: every chunk lies in one block (block_size >= the chunk)
   if ((1 << bs_log2) >= chunk_tokens(D, MH))
     return launch_decode<D, GP, MH, true>(q, out, k_cache, v_cache, num_q_heads, num_kv_heads,
                                           bs_log2, batch, context_lens, block_tables,
-                                          table_stride, scale, num_workers, workspace, stream);
+                                          table_stride, scale, num_workers, workspace, cos_sin,
+                                          max_position, stream);
   return launch_decode<D, GP, MH, false>(q, out, k_cache, v_cache, num_q_heads, num_kv_heads,
                                          bs_log2, batch, context_lens, block_tables,
-                                         table_stride, scale, num_workers, workspace, stream);
+                                         table_stride, scale, num_workers, workspace, cos_sin,
+                                         max_position, stream);
 }
 
 template <int D, int MH>
@@ -610,11 +640,12 @@ hipError_t launch_decode_gp(int GP, const void* q, void* out, const void* k_cach
                             const void* v_cache, int num_q_heads, int num_kv_heads, int bs_log2,
                             int batch, const int32_t* context_lens, const int32_t* block_tables,
                             int table_stride, float scale, int num_workers, void* workspace,
-                            hipStream_t stream) {
+                            const float* cos_sin, int max_position, hipStream_t stream) {
 #define PKV_DEC(GP_)                                                                         \
   return launch_decode_bs<D, GP_, MH>(q, out, k_cache, v_cache, num_q_heads, num_kv_heads, \
                                       bs_log2, batch, context_lens, block_tables,          \
-                                      table_stride, scale, num_workers, workspace, stream)
+                                      table_stride, scale, num_workers, workspace, cos_sin, \
+                                      max_position, stream)
   switch (GP) {
     case 1: PKV_DEC(1);
     case 2: PKV_DEC(2);
@@ -638,13 +669,15 @@ hipError_t launch_paged_decode_bf16(int head_dim, const void* q, void* out, cons
                                     const void* v_cache, int num_q_heads, int num_kv_heads,
                                     int bs_log2, int batch, const int32_t* context_lens,
                                     const int32_t* block_tables, int table_stride, float scale,
-                                    int num_workers, void* workspace, hipStream_t stream) {
+                                    int num_workers, void* workspace, const float* cos_sin,
+                                    int max_position, hipStream_t stream) {
   const int GP = heads_per_stream(num_q_heads / num_kv_heads);
   const int MH = kv_heads_per_stream(head_dim, num_kv_heads);
 #define PKV_DEC(D_, MH_)                                                                      \
   return launch_decode_gp<D_, MH_>(GP, q, out, k_cache, v_cache, num_q_heads, num_kv_heads, \
                                    bs_log2, batch, context_lens, block_tables, table_stride, \
-                                   scale, num_workers, workspace, stream)
+                                   scale, num_workers, workspace, cos_sin, max_position,     \
+                                   stream)
   if (head_dim == 128) {
     switch (MH) {
       case 1: PKV_DEC(128, 1);

@@ -146,13 +146,14 @@ __device__ __forceinline__ void dma16_ptr(const void* p, uint32_t lds) {
                : "memory", "m0");
 }
 
-template <int D, int GP, bool BIG_BLOCK>
+template <int D, int GP, bool BIG_BLOCK, bool ROT>
 __global__ __launch_bounds__(256, 2) void paged_prefill_bf16_kernel(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
     const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
     const int32_t* __restrict__ cu_seqlens_q, const int32_t* __restrict__ cu_seqlens_k,
     const int32_t* __restrict__ block_tables, int table_stride, int Hq, int Hkv, int G,
-    int bs_log2, float scale_log2, int batch, int max_tiles) {
+    int bs_log2, float scale_log2, int batch, int max_tiles, const float* __restrict__ cos_sin,
+    int max_position) {
   static_assert(D == 64 || D == 128, "head_dim");
   constexpr int BM_TOK = 128 / GP;  // tokens per workgroup tile
   constexpr int BN = 64;            // keys per K/V tile
@@ -200,6 +201,22 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_bf16_kernel(
   const int hq = kvh * G + head;
   const int diag = Lk - Lq + tok;  // last visible key of this row (any value is fine if invalid)
 
+  // rotary: cosines and sines of this row's position for the elements this lane holds
+  // in k-steps ks < KS/2 (loaded first, independent of q)
+  constexpr int KR = ROT ? KS / 2 : 1;
+  f32x4_t rc[KR][2], rs[KR][2];
+  if constexpr (ROT) {
+    const float* cs =
+        cos_sin + static_cast<int64_t>(min(max(diag, 0), max_position - 1)) * D + 8 * hi;
+#pragma unroll
+    for (int ks = 0; ks < KR; ++ks)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        rc[ks][h2] = *reinterpret_cast<const f32x4_t*>(cs + ks * 16 + 4 * h2);
+        rs[ks][h2] = *reinterpret_cast<const f32x4_t*>(cs + D / 2 + ks * 16 + 4 * h2);
+      }
+  }
+
   // q row as the S^T MFMA B operand: lane holds d = ks*16 + 8*hi .. +8
   bf16x8_t qb[KS];
 #pragma unroll
@@ -209,6 +226,23 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_bf16_kernel(
       w = *reinterpret_cast<const u32x4_t*>(
           q + (static_cast<int64_t>(q_begin + tok) * Hq + hq) * D + ks * 16 + 8 * hi);
     qb[ks] = __builtin_bit_cast(bf16x8_t, w);
+  }
+  if constexpr (ROT) {
+    // element d of k-step ks (d = ks*16 + 8*hi + e) pairs with d + D/2, which this lane
+    // holds in k-step ks + KS/2; rows past the sequence hold zeros and stay zero
+#pragma unroll
+    for (int ks = 0; ks < KR; ++ks) {
+      const float c[8] = {rc[ks][0][0], rc[ks][0][1], rc[ks][0][2], rc[ks][0][3],
+                          rc[ks][1][0], rc[ks][1][1], rc[ks][1][2], rc[ks][1][3]};
+      const float sn[8] = {rs[ks][0][0], rs[ks][0][1], rs[ks][0][2], rs[ks][0][3],
+                           rs[ks][1][0], rs[ks][1][1], rs[ks][1][2], rs[ks][1][3]};
+      const u32x4_t xv = __builtin_bit_cast(u32x4_t, qb[ks]);
+      const u32x4_t yv = __builtin_bit_cast(u32x4_t, qb[ks + KS / 2]);
+      uint32_t x[4] = {xv[0], xv[1], xv[2], xv[3]}, y[4] = {yv[0], yv[1], yv[2], yv[3]};
+      rope8_bf16(x, y, c, sn);
+      qb[ks] = __builtin_bit_cast(bf16x8_t, u32x4_t{x[0], x[1], x[2], x[3]});
+      qb[ks + KS / 2] = __builtin_bit_cast(bf16x8_t, u32x4_t{y[0], y[1], y[2], y[3]});
+    }
   }
 
   // keys the workgroup needs: up to the diagonal of its last valid token
@@ -423,14 +457,18 @@ static void launch_prefill(dim3 grid, hipStream_t stream, const void* q, void* o
                            const void* kc, const void* vc, const int32_t* cu_q,
                            const int32_t* cu_k, const int32_t* tables, int stride, int Hq,
                            int Hkv, int G, int bs_log2, float scale_log2, int batch,
-                           int max_tiles) {
+                           int max_tiles, const float* cos_sin, int max_position) {
   // blocks of at least 64 tokens hold a whole 64-key tile
-  auto kernel = bs_log2 >= 6 ? paged_prefill_bf16_kernel<D, GP, true>
-                             : paged_prefill_bf16_kernel<D, GP, false>;
+  auto kernel = cos_sin != nullptr
+                    ? (bs_log2 >= 6 ? paged_prefill_bf16_kernel<D, GP, true, true>
+                                    : paged_prefill_bf16_kernel<D, GP, false, true>)
+                    : (bs_log2 >= 6 ? paged_prefill_bf16_kernel<D, GP, true, false>
+                                    : paged_prefill_bf16_kernel<D, GP, false, false>);
   hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<uint16_t*>(out),
                      static_cast<const uint16_t*>(kc), static_cast<const uint16_t*>(vc), cu_q,
-                     cu_k, tables, stride, Hq, Hkv, G, bs_log2, scale_log2, batch, max_tiles);
+                     cu_k, tables, stride, Hq, Hkv, G, bs_log2, scale_log2, batch, max_tiles,
+                     cos_sin, max_position);
 }
 
 hipError_t launch_paged_prefill_bf16(int head_dim, const void* q, void* out, const void* k_cache,
@@ -438,7 +476,7 @@ hipError_t launch_paged_prefill_bf16(int head_dim, const void* q, void* out, con
                                      int bs_log2, int batch, int max_seqlen_q,
                                      const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                                      const int32_t* block_tables, int table_stride, float scale,
-                                     hipStream_t stream) {
+                                     const float* cos_sin, int max_position, hipStream_t stream) {
   const int G = num_q_heads / num_kv_heads;
   if (G > 128) return hipErrorInvalidConfiguration;
   const int GP = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : G <= 8 ? 8 : G <= 16 ? 16 : G <= 32
@@ -453,7 +491,7 @@ hipError_t launch_paged_prefill_bf16(int head_dim, const void* q, void* out, con
 #define PKV_PF(D_, GP_)                                                                       \
   launch_prefill<D_, GP_>(grid, stream, q, out, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k, \
                           block_tables, table_stride, num_q_heads, num_kv_heads, G, bs_log2,  \
-                          scale_log2, batch, max_tiles)
+                          scale_log2, batch, max_tiles, cos_sin, max_position)
 #define PKV_PF_GP(D_)                                  \
   switch (GP) {                                        \
     case 1: PKV_PF(D_, 1); break;                      \

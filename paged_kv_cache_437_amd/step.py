@@ -44,10 +44,13 @@ def _fill_bits(t: torch.Tensor, bits: int) -> None:
 
 class DeviceStep:
     def __init__(self, wl, device="cuda", stale: str | None = "nan", table_pad: int = -1,
-                 num_workers: int = 0, plan=None):
+                 num_workers: int = 0, plan=None, rotary: torch.Tensor | None = None):
+        """``rotary``: a rotary_table; K is then rotated at each token's position as it
+        is written (history and step alike) and queries are rotated at theirs."""
         self.wl = wl
         self.device = torch.device(device)
         self.num_workers = num_workers
+        self.rotary = rotary
         pool = BlockPool(wl.num_blocks, wl.free_order)
         self.plan = plan if plan is not None else plan_step(wl.seqs, wl.block_size, pool,
                                                             table_pad)
@@ -76,16 +79,18 @@ class DeviceStep:
 
         dev = self.device
         hk, hv = rows(p.history_seq, p.history_pos)
+        i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
         if len(p.history_slots):
             store_kvcache(to_device_values(hk, dev), to_device_values(hv, dev), self.k_cache,
-                          self.v_cache, torch.from_numpy(p.history_slots).to(dev))
+                          self.v_cache, torch.from_numpy(p.history_slots).to(dev),
+                          positions=i32(p.history_pos), rotary=rotary)
         del hk, hv
         sk, sv = rows(p.step_seq, p.step_pos)
         self.k_new = to_device_values(sk, dev)
         self.v_new = to_device_values(sv, dev)
         self.slot_mapping = torch.from_numpy(p.step_slots).to(dev)
+        self.positions = i32(p.step_pos)
 
-        i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
         self.q_prefill = self.q_decode = None
         if p.prefill:
             self.q_prefill = to_device_values(np.concatenate([wl.q[i] for i in p.prefill]), dev)
@@ -104,7 +109,8 @@ class DeviceStep:
 
     # the three calls of the hot path, separately (for per-kernel timing) and together
     def store(self):
-        store_kvcache(self.k_new, self.v_new, self.k_cache, self.v_cache, self.slot_mapping)
+        store_kvcache(self.k_new, self.v_new, self.k_cache, self.v_cache, self.slot_mapping,
+                      positions=self.positions, rotary=self.rotary)
 
     def prefill(self):
         if self.q_prefill is None:
@@ -112,7 +118,8 @@ class DeviceStep:
         p = self.plan
         return paged_prefill(self.q_prefill, self.k_cache, self.v_cache, self.cu_seqlens_q,
                              self.cu_seqlens_k, self.prefill_tables, p.max_seqlen_q,
-                             p.max_seqlen_k, self.wl.scale, out=self.out_prefill)
+                             p.max_seqlen_k, self.wl.scale, out=self.out_prefill,
+                             rotary=self.rotary)
 
     def decode(self):
         if self.q_decode is None:
@@ -121,7 +128,7 @@ class DeviceStep:
         return paged_decode(self.q_decode, self.k_cache, self.v_cache, self.decode_tables,
                             self.context_lens, p.max_context_len, self.wl.scale,
                             num_workers=self.num_workers, out=self.out_decode,
-                            workspace=self.workspace)
+                            workspace=self.workspace, rotary=self.rotary)
 
     def run(self):
         self.store()
