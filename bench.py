@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only the prefill leg (for profiling it alone)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the graph-replay and rotary comparisons (for profiling the "
+                         "decode step alone)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="rough CPU budget of the oracle baseline sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -296,7 +299,7 @@ def main():
     d_bytes = decode_bytes(wl, plan)
     s_bytes = store_bytes(wl, n_new)
     value = (d_bytes + s_bytes) / (ms_per_step * 1e-3) / 1e9
-    graph_big = graph_step(torch, pkv, step, wl, args)
+    graph_big = None if args.no_extras else graph_step(torch, pkv, step, wl, args)
     decode_kernels = {k: v for k, v in kernels.items() if "decode" in k}
     dom_name = max(decode_kernels, key=lambda k: decode_kernels[k]["total_ms"])
     dom = decode_kernels[dom_name]
@@ -337,32 +340,36 @@ def main():
         },
         "kernels": {k: {"launches": v["launches"], "avg_ms": round(v["avg_ms"], 5)}
                     for k, v in kernels.items()},
-        "graph_step": {
+    }
+    if not args.no_extras:
+        result["graph_step"] = {
             "what": "decode step (KV write + decode) eager vs replayed from a HIP graph",
             "this_workload": graph_big,
             "launch_bound": small_decode_graph(torch, pkv, workloads, DeviceStep, args),
-        },
-    }
+        }
 
     # ---- the same decode step with rotary position embedding fused in (K rotated in
     # the KV write, the queries in the decode kernel)
-    table = pkv.rotary_table(4096, wl.head_dim)
-    rstep = DeviceStep(wl, device="cuda", stale="nan", rotary=table)
-    for _ in range(args.warmup):
-        rstep.run()
-    r_ms, _, _ = timed_steps(torch, pkv, rstep.run, args.steps, kernel_events=False)
-    result["rotary"] = {"decode_ms_per_step": round(r_ms / args.steps, 5),
-                        "decode_value": round((d_bytes + s_bytes) / (r_ms / args.steps * 1e-3)
-                                              / 1e9, 2), "unit": "GB/s"}
-    del rstep
+    if not args.no_extras:
+        table = pkv.rotary_table(4096, wl.head_dim)
+        rstep = DeviceStep(wl, device="cuda", stale="nan", rotary=table)
+        for _ in range(args.warmup):
+            rstep.run()
+        r_ms, _, _ = timed_steps(torch, pkv, rstep.run, args.steps, kernel_events=False)
+        result["rotary"] = {"decode_ms_per_step": round(r_ms / args.steps, 5),
+                            "decode_value": round((d_bytes + s_bytes)
+                                                  / (r_ms / args.steps * 1e-3) / 1e9, 2),
+                            "unit": "GB/s"}
+        del rstep
 
     # ---- varlen causal prefill, reported beside the decode line
     if not args.no_prefill:
         del step
         torch.cuda.empty_cache()
         result["prefill"] = prefill_leg(torch, pkv, workloads, DeviceStep, args)
-        result["rotary"]["prefill_tflops"] = prefill_leg(torch, pkv, workloads, DeviceStep, args,
-                                                         rotary=True)["achieved"]
+        if not args.no_extras:
+            result["rotary"]["prefill_tflops"] = prefill_leg(torch, pkv, workloads, DeviceStep,
+                                                             args, rotary=True)["achieved"]
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
