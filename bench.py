@@ -217,6 +217,30 @@ def small_decode_graph(torch, pkv, workloads, DeviceStep, args) -> dict:
     return out
 
 
+def mixed_leg(torch, pkv, workloads, DeviceStep, args) -> dict:
+    """A step whose batch mixes both phases - 32 decode sequences (ctx uniform
+    [512, 4096]) and 8 prompts (lengths uniform [128, 2048]), 32 q / 32 kv heads,
+    head_dim 128, block_size 256 - with prefill and decode as two launches and as one."""
+    import numpy as np
+    from workloads import SeqSpec
+    rng = np.random.default_rng(args.seed + 100)
+    seqs = [SeqSpec("decode", int(L), 1) for L in rng.integers(512, 4096, 32, endpoint=True)]
+    seqs += [SeqSpec("prefill", int(L), int(L)) for L in rng.integers(128, 2048, 8, endpoint=True)]
+    wm = workloads.custom("mixed_bf16", "bf16", 32, 32, 128, 256, seqs, seed=args.seed + 100)
+    st = DeviceStep(wm, device="cuda", stale="nan")
+    two = lambda: (st.prefill(), st.decode())
+    for _ in range(args.warmup):
+        two()
+        st.mixed()
+    t_ms, _, _ = timed_steps(torch, pkv, two, args.steps, kernel_events=False)
+    m_ms, _, _ = timed_steps(torch, pkv, st.mixed, args.steps, kernel_events=False)
+    del st
+    return {"workload": "32 decode seqs ctx U[512, 4096] + 8 prompts U[128, 2048], 32 q / 32 kv "
+                        "heads, head_dim 128, block_size 256 (attention only, KV written before)",
+            "two_launches_ms": round(t_ms / args.steps, 5),
+            "one_launch_ms": round(m_ms / args.steps, 5)}
+
+
 def prefill_leg(torch, pkv, workloads, DeviceStep, args, rotary: bool = False) -> dict:
     """Varlen causal prefill (16 prompts, lengths uniform on [128, 2048]) in TFLOP/s;
     with ``rotary`` the queries are rotated in the kernel's prologue (and K on write)."""
@@ -370,6 +394,7 @@ def main():
         if not args.no_extras:
             result["rotary"]["prefill_tflops"] = prefill_leg(torch, pkv, workloads, DeviceStep,
                                                              args, rotary=True)["achieved"]
+            result["mixed_step"] = mixed_leg(torch, pkv, workloads, DeviceStep, args)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

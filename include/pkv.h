@@ -193,6 +193,28 @@ pkv_status pkv_paged_decode_rotary(const pkv_cache* cache, const void* q, void* 
                                    int32_t num_workers, const pkv_rotary* rotary,
                                    hipStream_t stream);
 
+/* One step's attention for a batch holding sequences in both phases (“深入 Nano-vLLM 推理引擎”,
+ * "Prefill and Decode" and the scheduler headings: the running batch mixes prompts
+ * being prefilled with sequences being decoded).  The prefill arguments are those of
+ * pkv_paged_prefill (for the prefill sequences), the decode arguments those of
+ * pkv_paged_decode (for the decode sequences, with its workspace and num_workers), and
+ * rotary is NULL or as in the _rotary calls.  Results are bit-identical to the two
+ * calls made one after the other.  For bf16 caches with block_size >= 64 and at most
+ * 8 q heads per kv head both passes run in one kernel launch (workgroups of the
+ * decode pass, then the prefill's work items, sharing the GPU) followed by the
+ * decode's merge kernel; other shapes, and steps with one phase empty, run the two
+ * passes one after the other.  Errors as in the two calls. */
+pkv_status pkv_mixed_attention(const pkv_cache* cache, int32_t num_q_heads, float scale,
+                               const void* q_prefill, void* out_prefill, int32_t prefill_batch,
+                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                               int32_t max_seqlen_q, int32_t max_seqlen_k,
+                               const int32_t* prefill_tables, int32_t prefill_table_stride,
+                               const void* q_decode, void* out_decode, int32_t decode_batch,
+                               const int32_t* context_lens, int32_t max_context_len,
+                               const int32_t* decode_tables, int32_t decode_table_stride,
+                               void* workspace, size_t workspace_bytes, int32_t num_workers,
+                               const pkv_rotary* rotary, hipStream_t stream);
+
 /* ---- Block manager: the host control plane that hands out block ids.
  * (“Nano-vLLM 引擎架构解析” section 3.2 "PagedAttention": a Block has an id, a
  * reference count and its token ids; the manager keeps a deque of free blocks and

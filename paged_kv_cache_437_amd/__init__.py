@@ -29,7 +29,7 @@ from . import _lib
 from ._lib import PkvError
 
 __all__ = ["store_kvcache", "paged_prefill", "paged_decode", "paged_decode_workspace_size",
-           "rotary_table", "PkvError", "version", "library_path", "timing_enable",
+           "mixed_attention", "rotary_table", "PkvError", "version", "library_path", "timing_enable",
            "timing_collect"]
 
 _DTYPES = {torch.float32: _lib.PKV_F32, torch.bfloat16: _lib.PKV_BF16}
@@ -208,3 +208,47 @@ def paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         _lib.check(lib.pkv_paged_decode_rotary(ctypes.byref(desc), *args, ctypes.byref(rot),
                                                _stream(k_cache.device)))
     return out
+
+
+def mixed_attention(k_cache: torch.Tensor, v_cache: torch.Tensor, scale: float,
+                    q_prefill: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                    cu_seqlens_k: torch.Tensor, prefill_tables: torch.Tensor, max_seqlen_q: int,
+                    max_seqlen_k: int, q_decode: torch.Tensor, decode_tables: torch.Tensor,
+                    context_lens: torch.Tensor, max_context_len: int, num_workers: int = 0,
+                    out_prefill: torch.Tensor | None = None,
+                    out_decode: torch.Tensor | None = None,
+                    workspace: torch.Tensor | None = None,
+                    rotary: torch.Tensor | None = None):
+    """Prefill of some sequences and decode of others in one call (one kernel launch for
+    the common bf16 shapes); returns (out_prefill, out_decode), bit-identical to
+    paged_prefill and paged_decode called one after the other."""
+    lib = _lib.load()
+    desc = _cache_desc(k_cache, v_cache)
+    hq = q_decode.shape[1] if q_decode.numel() else q_prefill.shape[1]
+    pb = cu_seqlens_q.numel() - 1
+    db = q_decode.shape[0]
+    if out_prefill is None:
+        out_prefill = torch.empty_like(q_prefill)
+    if out_decode is None:
+        out_decode = torch.empty_like(q_decode)
+    need = lib.pkv_paged_decode_workspace_size(ctypes.byref(desc), hq, max(db, 1),
+                                               int(max(max_context_len, 1)), int(num_workers))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=k_cache.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ptr = lambda t, name, dt: _dev(t, name, dt, k_cache) if t.numel() else None
+    rot = _rotary(rotary, k_cache)
+    _lib.check(lib.pkv_mixed_attention(
+        ctypes.byref(desc), hq, float(scale),
+        ptr(q_prefill, "q_prefill", k_cache.dtype), ptr(out_prefill, "out_prefill", k_cache.dtype),
+        pb, _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32, k_cache),
+        _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32, k_cache), int(max_seqlen_q),
+        int(max_seqlen_k), ptr(prefill_tables, "prefill_tables", torch.int32),
+        prefill_tables.shape[1] if prefill_tables.dim() == 2 else 0,
+        ptr(q_decode, "q_decode", k_cache.dtype), ptr(out_decode, "out_decode", k_cache.dtype),
+        db, ptr(context_lens, "context_lens", torch.int32), int(max_context_len),
+        ptr(decode_tables, "decode_tables", torch.int32),
+        decode_tables.shape[1] if decode_tables.dim() == 2 else 0, ws_ptr, ws_bytes,
+        int(num_workers), None if rot is None else ctypes.byref(rot), _stream(k_cache.device)))
+    return out_prefill, out_decode

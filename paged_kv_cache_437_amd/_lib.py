@@ -19,6 +19,7 @@ EXPORTED = (
     "pkv_store_kvcache", "pkv_paged_prefill", "pkv_paged_decode_workspace_size",
     "pkv_paged_decode", "pkv_status_string", "pkv_last_error", "pkv_version",
     "pkv_store_kvcache_rotary", "pkv_paged_prefill_rotary", "pkv_paged_decode_rotary",
+    "pkv_mixed_attention",
     "pkv_timing_enable", "pkv_timing_collect",
     "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_num_free", "pkv_bm_ref_count",
     "pkv_bm_add_sequence", "pkv_bm_remove_sequence", "pkv_bm_can_allocate", "pkv_bm_allocate",
@@ -90,6 +91,9 @@ def load() -> ctypes.CDLL:
     lib.pkv_paged_decode_rotary.argtypes = [cache_p, P, P, I, I, P, I, P, I, ctypes.c_float, P,
                                             ctypes.c_size_t, I, rot_p, P]
     lib.pkv_paged_decode_rotary.restype = I
+    lib.pkv_mixed_attention.argtypes = [cache_p, I, ctypes.c_float, P, P, I, P, P, I, I, P, I,
+                                        P, P, I, P, I, P, I, P, ctypes.c_size_t, I, rot_p, P]
+    lib.pkv_mixed_attention.restype = I
     lib.pkv_status_string.argtypes = [I]
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.pkv_last_error.argtypes = []

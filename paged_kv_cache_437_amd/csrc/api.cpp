@@ -154,7 +154,7 @@ pkv_status prefill_impl(const pkv_cache* cache, const void* q, void* out, int32_
                         int32_t batch, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                         int32_t max_seqlen_q, int32_t max_seqlen_k, const int32_t* block_tables,
                         int32_t block_table_stride, float scale, const pkv_rotary* rot,
-                        hipStream_t stream) {
+                        hipStream_t stream, bool dry = false) {
   pkv_status st = check_cache(cache);
   if (st != PKV_OK) return st;
   if ((st = check_heads(cache, num_q_heads)) != PKV_OK) return st;
@@ -174,6 +174,7 @@ pkv_status prefill_impl(const pkv_cache* cache, const void* q, void* out, int32_
                 block_table_stride, static_cast<long long>(need));
   if (!(scale > 0.f) || !std::isfinite(scale))
     return fail(PKV_ERR_INVALID, "scale %g must be finite and positive", scale);
+  if (dry) return PKV_OK;
   const int bs_log2 = log2_exact(cache->block_size);
   const float* cs = rot != nullptr ? rot->cos_sin : nullptr;
   const int max_pos = rot != nullptr ? rot->max_position : 0;
@@ -237,7 +238,7 @@ pkv_status decode_impl(const pkv_cache* cache, const void* q, void* out, int32_t
                        int32_t batch, const int32_t* context_lens, int32_t max_context_len,
                        const int32_t* block_tables, int32_t block_table_stride, float scale,
                        void* workspace, size_t workspace_bytes, int32_t num_workers,
-                       const pkv_rotary* rot, hipStream_t stream) {
+                       const pkv_rotary* rot, hipStream_t stream, bool dry = false) {
   pkv_status st = check_cache(cache);
   if (st != PKV_OK) return st;
   if ((st = check_heads(cache, num_q_heads)) != PKV_OK) return st;
@@ -261,6 +262,7 @@ pkv_status decode_impl(const pkv_cache* cache, const void* q, void* out, int32_t
                                                     num_workers);
   if (ws > 0 && (workspace == nullptr || workspace_bytes < ws))
     return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, ws);
+  if (dry) return PKV_OK;
   const int bs_log2 = log2_exact(cache->block_size);
   const float* cs = rot != nullptr ? rot->cos_sin : nullptr;
   const int max_pos = rot != nullptr ? rot->max_position : 0;
@@ -306,3 +308,44 @@ pkv_status pkv_paged_decode_rotary(const pkv_cache* cache, const void* q, void* 
 }
 
 }  // extern "C"
+
+pkv_status pkv_mixed_attention(const pkv_cache* cache, int32_t num_q_heads, float scale,
+                               const void* q_prefill, void* out_prefill, int32_t prefill_batch,
+                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                               int32_t max_seqlen_q, int32_t max_seqlen_k,
+                               const int32_t* prefill_tables, int32_t prefill_table_stride,
+                               const void* q_decode, void* out_decode, int32_t decode_batch,
+                               const int32_t* context_lens, int32_t max_context_len,
+                               const int32_t* decode_tables, int32_t decode_table_stride,
+                               void* workspace, size_t workspace_bytes, int32_t num_workers,
+                               const pkv_rotary* rotary, hipStream_t stream) {
+  pkv_status st;
+  if (rotary != nullptr && (st = check_rotary(cache, rotary)) != PKV_OK) return st;
+  if ((st = prefill_impl(cache, q_prefill, out_prefill, num_q_heads, prefill_batch,
+                         cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, prefill_tables,
+                         prefill_table_stride, scale, rotary, stream, true)) != PKV_OK)
+    return st;
+  if ((st = decode_impl(cache, q_decode, out_decode, num_q_heads, decode_batch, context_lens,
+                        max_context_len, decode_tables, decode_table_stride, scale, workspace,
+                        workspace_bytes, num_workers, rotary, stream, true)) != PKV_OK)
+    return st;
+  if (cache->dtype == PKV_BF16 && prefill_batch > 0 && max_seqlen_q > 0 && decode_batch > 0) {
+    const hipError_t e = pkv::launch_mixed_attention_bf16(
+        cache->head_dim, cache->k_cache, cache->v_cache, num_q_heads, cache->num_kv_heads,
+        log2_exact(cache->block_size), scale, q_prefill, out_prefill, prefill_batch,
+        max_seqlen_q, cu_seqlens_q, cu_seqlens_k, prefill_tables, prefill_table_stride, q_decode,
+        out_decode, decode_batch, context_lens, decode_tables, decode_table_stride, num_workers,
+        workspace, rotary != nullptr ? rotary->cos_sin : nullptr,
+        rotary != nullptr ? rotary->max_position : 0, stream);
+    if (e != hipErrorNotSupported) return launched(e, "mixed_attention");
+  }
+  // shapes the single launch does not cover (and steps with one phase only): the two
+  // passes one after the other on the same stream
+  if ((st = prefill_impl(cache, q_prefill, out_prefill, num_q_heads, prefill_batch,
+                         cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, prefill_tables,
+                         prefill_table_stride, scale, rotary, stream)) != PKV_OK)
+    return st;
+  return decode_impl(cache, q_decode, out_decode, num_q_heads, decode_batch, context_lens,
+                     max_context_len, decode_tables, decode_table_stride, scale, workspace,
+                     workspace_bytes, num_workers, rotary, stream);
+}

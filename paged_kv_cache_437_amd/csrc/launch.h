@@ -49,6 +49,23 @@ hipError_t launch_paged_decode_bf16(int head_dim, const void* q, void* out, cons
                                     int num_workers, void* workspace, const float* cos_sin,
                                     int max_position, hipStream_t stream);
 
+// The worker count the bf16 decode picks when asked for 0 (auto).
+int paged_decode_bf16_workers(int head_dim, int num_q_heads, int num_kv_heads, int bs_log2);
+
+// Prefill of some sequences and decode of others in one launch (bf16, block_size >= 64,
+// at most 8 q heads per kv head), then the decode's merge kernel; the decode part is
+// the same work division as launch_paged_decode_bf16 with the same worker count, so
+// results are bit-identical to the two separate launches.  Returns
+// hipErrorNotSupported for shapes outside that set (the caller launches separately).
+hipError_t launch_mixed_attention_bf16(
+    int head_dim, const void* k_cache, const void* v_cache, int num_q_heads, int num_kv_heads,
+    int bs_log2, float scale, const void* q_prefill, void* out_prefill, int prefill_batch,
+    int max_seqlen_q, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+    const int32_t* prefill_tables, int prefill_stride, const void* q_decode, void* out_decode,
+    int decode_batch, const int32_t* context_lens, const int32_t* decode_tables,
+    int decode_stride, int num_workers, void* workspace, const float* cos_sin,
+    int max_position, hipStream_t stream);
+
 // bf16 varlen causal prefill on MFMA (one launch).  With cos_sin non-null, every query
 // row is rotated at its position (rotary table [max_position][head_dim] fp32).
 hipError_t launch_paged_prefill_bf16(int head_dim, const void* q, void* out, const void* k_cache,

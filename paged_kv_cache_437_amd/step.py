@@ -13,7 +13,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import paged_decode, paged_decode_workspace_size, paged_prefill, store_kvcache
+from . import (mixed_attention, paged_decode, paged_decode_workspace_size, paged_prefill,
+               store_kvcache)
 from .control import BlockPool, plan_step
 
 __all__ = ["DeviceStep", "to_device_values", "STALE_BITS"]
@@ -134,6 +135,25 @@ class DeviceStep:
         self.store()
         self.prefill()
         self.decode()
+        return self
+
+    def mixed(self):
+        """Prefill and decode of the step in one call (one launch for the common shapes)."""
+        if self.q_prefill is None or self.q_decode is None:
+            self.prefill()
+            self.decode()
+            return
+        p = self.plan
+        mixed_attention(self.k_cache, self.v_cache, self.wl.scale, self.q_prefill,
+                        self.cu_seqlens_q, self.cu_seqlens_k, self.prefill_tables,
+                        p.max_seqlen_q, p.max_seqlen_k, self.q_decode, self.decode_tables,
+                        self.context_lens, p.max_context_len, num_workers=self.num_workers,
+                        out_prefill=self.out_prefill, out_decode=self.out_decode,
+                        workspace=self.workspace, rotary=self.rotary)
+
+    def run_mixed(self):
+        self.store()
+        self.mixed()
         return self
 
     def outputs_numpy(self) -> dict:
