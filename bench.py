@@ -37,7 +37,7 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
 # rocprofv3 FETCH_SIZE / WRITE_SIZE summary of the decode kernel, with the hash of the
 # sources it was taken on (traffic is reported only while they are unchanged)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "paged_decode__decode_mha_bf16__traffic.txt")
-DECODE_SOURCES = ("paged_decode.hip", "decode_plan.h", "device.h")
+DECODE_SOURCES = ("paged_decode.hip", "decode_kernel.h", "decode_plan.h", "device.h")
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (256 CUs x 2.4 GHz x 4096 flop/clk/CU)
 
 

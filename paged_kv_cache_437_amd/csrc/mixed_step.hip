@@ -55,7 +55,9 @@ hipError_t launch_mixed_attention_bf16(
                                 : paged_decode_bf16_workers(head_dim, num_q_heads, num_kv_heads,
                                                             bs_log2);
   const DecodeWorkspace ws = carve_decode_workspace(workspace, decode_batch, W, MH * GP);
-  const int n_decode_wg = (W + 3) / 4;
+  // a multiple of 8 (the surplus workgroups have no worker and leave at once), so the
+  // prefill's item w sits on the XCD that w mod 8 names
+  const int n_decode_wg = ((W + 3) / 4 + kXcds - 1) / kXcds * kXcds;
   const int bm_tok = 128 / GP;
   const int max_tiles = (max_seqlen_q + bm_tok - 1) / bm_tok;
   const int64_t slots = static_cast<int64_t>(prefill_batch) * num_kv_heads * max_tiles;

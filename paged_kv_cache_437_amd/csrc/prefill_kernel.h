@@ -33,7 +33,11 @@
 // Work order: workgroups take the (sequence, kv head, q tile) items by tile rank
 // counted from each sequence's last (heaviest) tile, so long causal tiles start
 // first; the grid is sized for the longest sequence and the slots past the real
-// items (shorter sequences have fewer tiles) come last and exit at once.
+// items (shorter sequences have fewer tiles) come last and exit at once.  When the kv
+// heads divide into eight groups, workgroup w takes its items from kv heads
+// congruent to w mod 8 only: workgroups are dispatched to the eight XCDs in turn, so
+// every K/V tile of a kv head is read through one XCD's L2, where the other q tiles
+// of its sequence find it again.
 #pragma once
 
 #include "device.h"
@@ -153,6 +157,8 @@ __device__ __forceinline__ void dma16_ptr(const void* p, uint32_t lds) {
 
 // One workgroup (one work item of the list) of the prefill pass; the kernels that run
 // it give it its index.
+constexpr int kXcds = 8;  // XCDs of the part; workgroups are dispatched to them in turn
+
 template <int D, int GP, bool BIG_BLOCK, bool ROT>
 __device__ __forceinline__ void prefill_workgroup(
     int wg, const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
@@ -184,8 +190,15 @@ __device__ __forceinline__ void prefill_workgroup(
   __shared__ __attribute__((aligned(1024))) char v_lds1[TB];
 
   int b = 0, kvh = 0, tile = 0;
-  if (!prefill_item(wg, batch, Hkv, BM_TOK, max_tiles, cu_seqlens_q, b, kvh, tile))
-    return;  // past the item list: uniform over the workgroup, before any barrier
+  if (Hkv % kXcds == 0) {
+    // the list restricted to kv heads kvh = wg % 8 + 8 m, m < Hkv / 8
+    if (!prefill_item(wg / kXcds, batch, Hkv / kXcds, BM_TOK, max_tiles, cu_seqlens_q, b, kvh,
+                      tile))
+      return;  // past the list: uniform over the workgroup, before any barrier
+    kvh = wg % kXcds + kXcds * kvh;
+  } else if (!prefill_item(wg, batch, Hkv, BM_TOK, max_tiles, cu_seqlens_q, b, kvh, tile)) {
+    return;
+  }
   const int q_begin = cu_seqlens_q[b];
   const int Lq = cu_seqlens_q[b + 1] - q_begin;
   const int Lk = cu_seqlens_k[b + 1] - cu_seqlens_k[b];
