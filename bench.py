@@ -217,6 +217,29 @@ def small_decode_graph(torch, pkv, workloads, DeviceStep, args) -> dict:
     return out
 
 
+def prefill_shapes(torch, pkv, workloads, DeviceStep, args) -> dict:
+    """Prefill TFLOP/s on the prefix-cached workload (64 sequences, 1024 shared prefix
+    tokens + 256 own, suffix queries only, 32/8 heads) and on long causal prompts
+    (4 x 8192 tokens, 32/8 heads), beside the varlen headline."""
+    from workloads import SeqSpec
+    out = {}
+    for name, wl in (("prefill_prefix_cached", workloads.prefill_prefix_cached(seed=args.seed)),
+                     ("causal_4x8192_32q8kv", workloads.custom(
+                         "long_bf16", "bf16", 32, 8, 128, 256,
+                         [SeqSpec("prefill", 8192, 8192)] * 4, seed=args.seed))):
+        st = DeviceStep(wl, device="cuda", stale=None)
+        st.run()
+        torch.cuda.synchronize()
+        _, _, pk = timed_steps(torch, pkv, st.prefill, 5, kernel_events=True)
+        pname = max((k for k in pk if "prefill" in k), key=lambda k: pk[k]["total_ms"])
+        tf = prefill_flops(wl, st.plan) / (pk[pname]["avg_ms"] * 1e-3) / 1e12
+        out[name] = {"avg_launch_ms": round(pk[pname]["avg_ms"], 5), "TFLOP/s": round(tf, 2),
+                     "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4)}
+        del st
+        torch.cuda.empty_cache()
+    return out
+
+
 def mixed_leg(torch, pkv, workloads, DeviceStep, args) -> dict:
     """A step whose batch mixes both phases - 32 decode sequences (ctx uniform
     [512, 4096]) and 8 prompts (lengths uniform [128, 2048]), 32 q / 32 kv heads,
@@ -395,6 +418,7 @@ def main():
             result["rotary"]["prefill_tflops"] = prefill_leg(torch, pkv, workloads, DeviceStep,
                                                              args, rotary=True)["achieved"]
             result["mixed_step"] = mixed_leg(torch, pkv, workloads, DeviceStep, args)
+            result["prefill_shapes"] = prefill_shapes(torch, pkv, workloads, DeviceStep, args)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
