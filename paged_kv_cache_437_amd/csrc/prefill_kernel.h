@@ -363,27 +363,43 @@ __device__ __forceinline__ void prefill_workgroup(
     // ---- S^T = K Q^T for 64 keys: s[sub][r] is key 32*sub + 8*(r/4) + 4*hi + r%4
     f32x16_t s[2];
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
+    for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[sub][r] = 0.f;
+    // the two 32-key blocks' MFMA chains alternate, and each k-step's two K operands
+    // are read while the previous k-step's MFMAs run (the group barriers pin that order:
+    // left to itself the scheduler waits on every read right before its MFMA)
+    auto kread = [&](int sub, int ks) -> bf16x8_t {
+      return __builtin_bit_cast(
+          bf16x8_t, *reinterpret_cast<const u32x4_t*>(kl + 32 * sub * RB + kaddr[ks]));
+    };
+    bf16x8_t ka[KS][2];
+    ka[0][0] = kread(0, 0);
+    ka[0][1] = kread(1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 0x100: LDS reads
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8_t ka = __builtin_bit_cast(
-            bf16x8_t, *reinterpret_cast<const u32x4_t*>(kl + 32 * sub * RB + kaddr[ks]));
-        s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[ks], s[sub], 0, 0, 0);
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + 1 < KS) {
+        ka[ks + 1][0] = kread(0, ks + 1);
+        ka[ks + 1][1] = kread(1, ks + 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
+      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks][0], qb[ks], s[0], 0, 0, 0);
+      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks][1], qb[ks], s[1], 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 0x008: MFMAs
     }
 
     // ---- causal mask on diagonal tiles (keys past Lk are past every diagonal too)
     if (t >= first_masked_tile) {
-      const int lim = diag - t * BN;  // key offsets <= lim are visible
+      // key offset 32*sub + 8*(r/4) + 4*hi + r%4 is visible when it is <= diag - t*BN;
+      // the lane's 4*hi moves to the right-hand side so every test is against a
+      // constant (no per-lane offsets held in registers across the loop)
+      const int lim = diag - t * BN - 4 * hi;
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kofs = 32 * sub + 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (kofs > lim) s[sub][r] = -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r)
+          if (32 * sub + 8 * (r >> 2) + (r & 3) > lim) s[sub][r] = -INFINITY;
     }
 
     // ---- online softmax in the log2 domain; the row max is this lane's 32 keys and
