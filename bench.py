@@ -19,8 +19,10 @@ metadata used) divided by the step time, timed without per-kernel events.
 HIP events recorded on its own stream around each launch, in a second timed pass
 over the same K steps.  ``prefill`` reports the varlen causal prefill (16 q /
 8 kv heads, 16 prompts of length uniform on [128, 2048]) in TFLOP/s over the
-unmasked causal pairs.  ``cpu_baseline`` times the CPU oracle on a bounded
-sample of the same decode workload, on this host's cores.
+unmasked causal pairs.  ``decode_large`` reports the large decode batch (256
+sequences, lognormal contexts, 32 q / 8 kv heads, pool at 60% of free memory) in
+GB/s.  ``cpu_baseline`` times the CPU oracle on a bounded sample of the same decode
+workload, on this host's cores.
 """
 from __future__ import annotations
 
@@ -240,6 +242,40 @@ def prefill_shapes(torch, pkv, workloads, DeviceStep, args) -> dict:
     return out
 
 
+def decode_large_leg(torch, pkv, workloads, DeviceStep, args) -> dict:
+    """The large decode batch: 256 sequences, ln(context) ~ N(ln 2048, 1) clipped to
+    [64, 16384], 32 q / 8 kv heads, head_dim 128, block_size 256, the pool sized to 60%
+    of free device memory with the used blocks scattered over it.  Reports the decode
+    kernel's algorithmic HBM rate (events around each launch) and the whole step's."""
+    free, _ = torch.cuda.mem_get_info()
+    bb = workloads.block_bytes(256, 8, 128, 2)
+    wl = workloads.decode_large(seed=args.seed, pool_blocks=int(0.6 * free // bb))
+    st = DeviceStep(wl, device="cuda", stale=None)
+    for _ in range(3):
+        st.run()
+    torch.cuda.synchronize()
+    steps = max(5, args.steps // 5)
+    ms, _, _ = timed_steps(torch, pkv, st.run, steps, kernel_events=False)
+    _, _, kernels = timed_steps(torch, pkv, st.run, steps, kernel_events=True)
+    d_bytes = decode_bytes(wl, st.plan)
+    s_bytes = store_bytes(wl, len(st.plan.step_slots))
+    dec = kernels["paged_decode"]
+    gbs = d_bytes / (dec["avg_ms"] * 1e-3) / 1e9
+    out = {"workload": "decode_large_bf16: 256 seqs, ln ctx ~ N(ln 2048, 1) clipped [64, 16384], "
+                       "32 q / 8 kv heads, head_dim 128, block_size 256, pool 60% of free HBM",
+           "sum_context": int(sum(s.context_len for s in wl.seqs)),
+           "pool_blocks": wl.num_blocks,
+           "decode_avg_launch_ms": round(dec["avg_ms"], 5),
+           "merge_avg_launch_ms": round(kernels.get("paged_decode_combine", {"avg_ms": 0.0})["avg_ms"], 5),
+           "algorithmic_bytes_per_launch": d_bytes,
+           "achieved": round(gbs, 2), "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+           "step_ms": round(ms / steps, 5),
+           "step_GB/s": round((d_bytes + s_bytes) / (ms / steps * 1e-3) / 1e9, 2)}
+    del st
+    torch.cuda.empty_cache()
+    return out
+
+
 def mixed_leg(torch, pkv, workloads, DeviceStep, args) -> dict:
     """A step whose batch mixes both phases - 32 decode sequences (ctx uniform
     [512, 4096]) and 8 prompts (lengths uniform [128, 2048]), 32 q / 32 kv heads,
@@ -419,6 +455,7 @@ def main():
                                                              args, rotary=True)["achieved"]
             result["mixed_step"] = mixed_leg(torch, pkv, workloads, DeviceStep, args)
             result["prefill_shapes"] = prefill_shapes(torch, pkv, workloads, DeviceStep, args)
+            result["decode_large"] = decode_large_leg(torch, pkv, workloads, DeviceStep, args)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

@@ -53,11 +53,12 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 // (1, 1) in bf16: v_dot2 with it adds a pair of bf16 values into an fp32 sum
 constexpr bf16x2_t kOnes = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
-__device__ __forceinline__ i16x4_t lds_read_tr16(const uint16_t* p) {
+// The pointer is cast to the LDS address space directly (not through an integer), so
+// the compiler sees the __shared__ object plus an offset and folds constant offsets
+// into the instruction's immediate field instead of keeping one address per offset.
+__device__ __forceinline__ i16x4_t lds_read_tr16(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) i16x4_t*)(
-          reinterpret_cast<__attribute__((address_space(3))) uint16_t*>(
-              reinterpret_cast<uintptr_t>(p))));
+      (__attribute__((address_space(3))) i16x4_t*)((const __attribute__((address_space(3))) char*)p));
 }
 
 // Workgroup -> work item.  Item i of the list ordered by q-tile rank counted from
@@ -451,9 +452,9 @@ __device__ __forceinline__ void prefill_workgroup(
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const i16x4_t lo4 =
-            lds_read_tr16(reinterpret_cast<const uint16_t*>(vl + ks * 16 * RB + vaddr[dt]));
+            lds_read_tr16(vl + ks * 16 * RB + vaddr[dt]);
         const i16x4_t hi4 =
-            lds_read_tr16(reinterpret_cast<const uint16_t*>(vl + ks * 16 * RB + vaddr8[dt]));
+            lds_read_tr16(vl + ks * 16 * RB + vaddr8[dt]);
         const u32x2_t lo = __builtin_bit_cast(u32x2_t, lo4);
         const u32x2_t hi2 = __builtin_bit_cast(u32x2_t, hi4);
         const u32x4_t va = {lo[0], lo[1], hi2[0], hi2[1]};
