@@ -45,12 +45,13 @@ int auto_workers() {
     cus = 256;
     per_cu = 2;
   }
-  // Waves per SIMD: one while each byte streamed costs little arithmetic (up to 2 q
+  // Waves per SIMD: one while each byte streamed costs little arithmetic (up to 4 q
   // heads per kv head), two beyond (the VALU then needs a second wave to hide behind).
   // Measured: more concurrent streams read HBM less efficiently, so the smallest count
-  // that keeps the arithmetic hidden is the fastest.  A whole number of workgroups per
-  // CU keeps the CUs evenly loaded.
-  w = std::min(kMaxAutoWorkers, cus * std::min(per_cu, GP <= 2 ? 1 : 2) * 4);
+  // that keeps the arithmetic hidden is the fastest (at 4 q heads per kv head one wave
+  // per SIMD is 4-13% faster than two; at 8, two are 8% faster).  A whole number of
+  // workgroups per CU keeps the CUs evenly loaded.
+  w = std::min(kMaxAutoWorkers, cus * std::min(per_cu, GP <= 4 ? 1 : 2) * 4);
   cached[dev].store(w, std::memory_order_relaxed);
   return w;
 }
