@@ -313,9 +313,18 @@ def prefill_leg(torch, pkv, workloads, DeviceStep, args, rotary: bool = False) -
     pname = max((k for k in pk if "prefill" in k), key=lambda k: pk[k]["total_ms"])
     flops = prefill_flops(wp, ps.plan)
     tflops = flops / (pk[pname]["avg_ms"] * 1e-3) / 1e12
+    # the KV write of all the prompts' tokens (HBM-bound at this size)
+    _, _, sk = timed_steps(torch, pkv, ps.store, max(5, args.steps // 5), kernel_events=True)
+    n_tok = len(ps.plan.step_slots)
+    sname = next(k for k in sk if k.startswith("store_kvcache"))  # with or without rotary
+    s_gbs = store_bytes(wp, n_tok) / (sk[sname]["avg_ms"] * 1e-3) / 1e9
     del ps
     torch.cuda.empty_cache()
     return {
+        "store_kvcache": {"tokens": n_tok, "bytes_per_launch": store_bytes(wp, n_tok),
+                          "kernel": sname, "avg_launch_ms": round(sk[sname]["avg_ms"], 5),
+                          "achieved": round(s_gbs, 2), "unit": "GB/s",
+                          "frac": round(s_gbs / HBM_PEAK_GBS, 4)},
         "workload": "prefill_varlen_bf16: 16 prompts, lengths uniform [128, 2048], "
                     "16 q / 8 kv heads, head_dim 128, block_size 256",
         "kernel": pname, "bound": "mfma", "achieved": round(tflops, 2),
@@ -431,6 +440,11 @@ def main():
             "launch_bound": small_decode_graph(torch, pkv, workloads, DeviceStep, args),
         }
 
+    # ---- the large decode batch, while device memory is still unfragmented (its pool
+    # takes 60% of it)
+    if not args.no_extras:
+        result["decode_large"] = decode_large_leg(torch, pkv, workloads, DeviceStep, args)
+
     # ---- the same decode step with rotary position embedding fused in (K rotated in
     # the KV write, the queries in the decode kernel)
     if not args.no_extras:
@@ -455,7 +469,6 @@ def main():
                                                              args, rotary=True)["achieved"]
             result["mixed_step"] = mixed_leg(torch, pkv, workloads, DeviceStep, args)
             result["prefill_shapes"] = prefill_shapes(torch, pkv, workloads, DeviceStep, args)
-            result["decode_large"] = decode_large_leg(torch, pkv, workloads, DeviceStep, args)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
