@@ -169,6 +169,31 @@ def test_decode_large_batch_short_contexts(pkv):
     _check_outputs(wl, _step(wl), oracle.run_step(wl))
 
 
+@pytest.mark.parametrize("case", ["bs16_gqa2", "bs256_kv8"])
+def test_prefill_many_sequences(pkv, case):
+    """Prefill batches of 300 short ragged prompts (empty ones, suffix-only ones over a
+    stored prefix) plus a few long ones: the work-item search scans several 64-sequence
+    chunks (past the ones it keeps in registers) and more than one group of q-tile
+    ranks.  Block size 16 (a tile spans blocks) with 2 q heads per kv head, and block
+    size 256 with 8 kv heads (items split over the XCDs)."""
+    rng = np.random.default_rng(33 if case == "bs16_gqa2" else 34)
+    S = workloads.SeqSpec
+    seqs = []
+    for k in range(300):
+        L = int(rng.integers(0, 160))
+        if k % 50 == 7:
+            L = 1100 + k
+        if k % 9 == 4 and L > 8:
+            seqs.append(S("prefill", L, int(rng.integers(1, L + 1))))  # suffix over a prefix
+        else:
+            seqs.append(S("prefill", L, L))
+    if case == "bs16_gqa2":
+        wl = workloads.custom("prefill_300_bs16", "bf16", 4, 2, 128, 16, seqs, seed=33)
+    else:
+        wl = workloads.custom("prefill_300_bs256", "bf16", 16, 8, 64, 256, seqs, seed=34)
+    _check_outputs(wl, _step(wl), oracle.run_step(wl))
+
+
 @pytest.mark.parametrize("workers", [1, 2, 3, 7, 61, 1000])
 def test_worker_count_agrees(pkv, workers):
     """Any division of the chunk list among workers (1 = every stream whole on one
