@@ -176,8 +176,15 @@ def cpu_baseline(wl, budget_s: float) -> dict:
         if time.perf_counter() - t0 >= budget_s:
             break
     secs = time.perf_counter() - t0
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f
+                              if ln.startswith("model name")), cpu_model)
+    except OSError:
+        pass
     return {"value": done_bytes / secs / 1e9, "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model,
             "sample": f"KV write of the {len(step_rows)} new tokens + float64 decode of "
                       f"{n} sequences ({passes} pass(es) over the {len(plan['decode'])}-sequence "
                       f"batch, {secs:.1f} s)"}

@@ -152,7 +152,9 @@ typedef __attribute__((address_space(3))) char lds_char;
 // LDS byte lds + 16 l.  Issued as inline assembly so the compiler does not track it:
 // the kernel orders these writes against the LDS reads itself (vmcnt(0) and a
 // barrier before a tile is read; a buffer is refilled only after every wave is done
-// with it).
+// with it).  The load takes its LDS address in m0, set in the same statement; in the
+// compiled prefill and mixed-step kernels no other instruction reads or writes m0, so
+// the clobber (which the compiler warns it may not preserve) loses nothing.
 __device__ __forceinline__ uint32_t lds_addr(const char* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_char*)p));
 }
