@@ -67,7 +67,7 @@ def test_config_parity(pkv, name):
 
 @pytest.mark.parametrize("seed", [1, 2])
 def test_config_parity_more_seeds(pkv, seed):
-    for name in ("tiny_mixed", "prefill_varlen"):
+    for name in ("tiny_mixed", "decode_mha", "prefill_varlen", "prefill_prefix_cached"):
         wl = workloads.by_name(name, seed=seed)
         _check_outputs(wl, _step(wl), oracle.run_step(wl))
 
