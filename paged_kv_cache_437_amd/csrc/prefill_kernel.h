@@ -240,50 +240,6 @@ __device__ __forceinline__ void prefill_workgroup(
   const int hq = kvh * G + head;
   const int diag = Lk - Lq + tok;  // last visible key of this row (any value is fine if invalid)
 
-  // rotary: cosines and sines of this row's position for the elements this lane holds
-  // in k-steps ks < KS/2 (loaded first, independent of q)
-  constexpr int KR = ROT ? KS / 2 : 1;
-  f32x4_t rc[KR][2], rs[KR][2];
-  if constexpr (ROT) {
-    const float* cs =
-        cos_sin + static_cast<int64_t>(min(max(diag, 0), max_position - 1)) * D + 8 * hi;
-#pragma unroll
-    for (int ks = 0; ks < KR; ++ks)
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        rc[ks][h2] = *reinterpret_cast<const f32x4_t*>(cs + ks * 16 + 4 * h2);
-        rs[ks][h2] = *reinterpret_cast<const f32x4_t*>(cs + D / 2 + ks * 16 + 4 * h2);
-      }
-  }
-
-  // q row as the S^T MFMA B operand: lane holds d = ks*16 + 8*hi .. +8
-  bf16x8_t qb[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    u32x4_t w = {0u, 0u, 0u, 0u};
-    if (row_valid)
-      w = *reinterpret_cast<const u32x4_t*>(
-          q + (static_cast<int64_t>(q_begin + tok) * Hq + hq) * D + ks * 16 + 8 * hi);
-    qb[ks] = __builtin_bit_cast(bf16x8_t, w);
-  }
-  if constexpr (ROT) {
-    // element d of k-step ks (d = ks*16 + 8*hi + e) pairs with d + D/2, which this lane
-    // holds in k-step ks + KS/2; rows past the sequence hold zeros and stay zero
-#pragma unroll
-    for (int ks = 0; ks < KR; ++ks) {
-      const float c[8] = {rc[ks][0][0], rc[ks][0][1], rc[ks][0][2], rc[ks][0][3],
-                          rc[ks][1][0], rc[ks][1][1], rc[ks][1][2], rc[ks][1][3]};
-      const float sn[8] = {rs[ks][0][0], rs[ks][0][1], rs[ks][0][2], rs[ks][0][3],
-                           rs[ks][1][0], rs[ks][1][1], rs[ks][1][2], rs[ks][1][3]};
-      const u32x4_t xv = __builtin_bit_cast(u32x4_t, qb[ks]);
-      const u32x4_t yv = __builtin_bit_cast(u32x4_t, qb[ks + KS / 2]);
-      uint32_t x[4] = {xv[0], xv[1], xv[2], xv[3]}, y[4] = {yv[0], yv[1], yv[2], yv[3]};
-      rope8_bf16(x, y, c, sn);
-      qb[ks] = __builtin_bit_cast(bf16x8_t, u32x4_t{x[0], x[1], x[2], x[3]});
-      qb[ks + KS / 2] = __builtin_bit_cast(bf16x8_t, u32x4_t{y[0], y[1], y[2], y[3]});
-    }
-  }
-
   // keys the workgroup needs: up to the diagonal of its last valid token
   const int tok_last = min(tok0 + BM_TOK, Lq) - 1;
   const int k_end = Lk - Lq + tok_last + 1;
@@ -337,6 +293,56 @@ __device__ __forceinline__ void prefill_workgroup(
     }
   };
 
+  // tile 0 goes out before the q rows: with blocks of 64 or more keys its block is the
+  // table's first entry, loaded with the sequence bounds rather than after them
+  int te_next = BIG_BLOCK ? table[0] : 0;
+  fetch(0, te_next, k_lds0, v_lds0);
+  if (BIG_BLOCK && n_kv > 1) te_next = tile_block(1);
+
+  // rotary: cosines and sines of this row's position for the elements this lane holds
+  // in k-steps ks < KS/2 (loaded first, independent of q)
+  constexpr int KR = ROT ? KS / 2 : 1;
+  f32x4_t rc[KR][2], rs[KR][2];
+  if constexpr (ROT) {
+    const float* cs =
+        cos_sin + static_cast<int64_t>(min(max(diag, 0), max_position - 1)) * D + 8 * hi;
+#pragma unroll
+    for (int ks = 0; ks < KR; ++ks)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        rc[ks][h2] = *reinterpret_cast<const f32x4_t*>(cs + ks * 16 + 4 * h2);
+        rs[ks][h2] = *reinterpret_cast<const f32x4_t*>(cs + D / 2 + ks * 16 + 4 * h2);
+      }
+  }
+
+  // q row as the S^T MFMA B operand: lane holds d = ks*16 + 8*hi .. +8
+  bf16x8_t qb[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    u32x4_t w = {0u, 0u, 0u, 0u};
+    if (row_valid)
+      w = *reinterpret_cast<const u32x4_t*>(
+          q + (static_cast<int64_t>(q_begin + tok) * Hq + hq) * D + ks * 16 + 8 * hi);
+    qb[ks] = __builtin_bit_cast(bf16x8_t, w);
+  }
+  if constexpr (ROT) {
+    // element d of k-step ks (d = ks*16 + 8*hi + e) pairs with d + D/2, which this lane
+    // holds in k-step ks + KS/2; rows past the sequence hold zeros and stay zero
+#pragma unroll
+    for (int ks = 0; ks < KR; ++ks) {
+      const float c[8] = {rc[ks][0][0], rc[ks][0][1], rc[ks][0][2], rc[ks][0][3],
+                          rc[ks][1][0], rc[ks][1][1], rc[ks][1][2], rc[ks][1][3]};
+      const float sn[8] = {rs[ks][0][0], rs[ks][0][1], rs[ks][0][2], rs[ks][0][3],
+                           rs[ks][1][0], rs[ks][1][1], rs[ks][1][2], rs[ks][1][3]};
+      const u32x4_t xv = __builtin_bit_cast(u32x4_t, qb[ks]);
+      const u32x4_t yv = __builtin_bit_cast(u32x4_t, qb[ks + KS / 2]);
+      uint32_t x[4] = {xv[0], xv[1], xv[2], xv[3]}, y[4] = {yv[0], yv[1], yv[2], yv[3]};
+      rope8_bf16(x, y, c, sn);
+      qb[ks] = __builtin_bit_cast(bf16x8_t, u32x4_t{x[0], x[1], x[2], x[3]});
+      qb[ks + KS / 2] = __builtin_bit_cast(bf16x8_t, u32x4_t{y[0], y[1], y[2], y[3]});
+    }
+  }
+
   // LDS read addresses (bytes within a tile): the K operand of k-step ks for this lane's
   // key row l32 (+32 rows for the second 32-key block: immediate), and the V^T operand
   // of head_dim tile dt for key row key_in (+16 rows per k-step, +8 for the second
@@ -364,9 +370,6 @@ __device__ __forceinline__ void prefill_workgroup(
   float m = -INFINITY;
   float l = 0.f;
 
-  int te_next = BIG_BLOCK ? tile_block(0) : 0;
-  fetch(0, te_next, k_lds0, v_lds0);
-  if (BIG_BLOCK && n_kv > 1) te_next = tile_block(1);
 
   auto step = [&](int t, const char* kl, const char* vl, char* kn, char* vn) {
     const bool has_next = t + 1 < n_kv;
