@@ -108,6 +108,12 @@ struct Cursor {
 
 // Loads per lane per chunk, for K and for V alike (each one 16 bytes)
 constexpr int kChunkLoads = 4;
+static_assert(kChunkLoads % 2 == 0, "P.V pairs a lane's tokens");
+
+// (1, 1) in bf16: v_dot2 with it adds a pair of bf16 values into an fp32 sum
+constexpr bf16x2_t kPairOnes = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+// lazy rescale: the running max moves only when a chunk exceeds it by more than 2^8
+constexpr float kRescaleSlack = 8.f;
 
 // One chunk's operands in registers: this lane's 16-byte pieces of K and V, one per
 // load instruction.
@@ -405,47 +411,58 @@ __device__ __forceinline__ void decode_workgroup(
   bool first_segment = true;  // the worker's first segment takes partial slot 2w
   int seg_k0 = cur.k;         // chunk at which the current segment started
 
-  // one chunk into the running state (registers only: no memory access)
+  // one chunk into the running state (registers only: no memory access).  The
+  // probabilities are rounded to bf16 once; P.V pairs this lane's tokens (same
+  // head_dim elements, tokens it and it+1) into bf16 dot products, and the sum takes the
+  // same rounded values.  The reference max a head's probabilities are taken against
+  // moves only when a chunk's max exceeds it by more than 2^8 (log2 domain), so most
+  // chunks skip the rescale of the running output; probabilities stay <= 2^8.
   auto accumulate = [&](const Cursor& x, const Buf& buf) {
     const int valid = x.L - x.k * CH;  // rows of the chunk inside the context
-    float p[GP][VIT];
+    bf16x2_t pk[GP][VIT / 2];
 #pragma unroll
     for (int h = 0; h < GP; ++h) {
       // scores of this lane's rows: the piece's dot product summed over the row's lanes
+      float s[VIT];
       float mx = -INFINITY;
 #pragma unroll
       for (int it = 0; it < VIT; ++it) {
         const float d = piece_sum<DCH>(dot_piece(qv[h], buf.k[it]));
-        p[h][it] = (it * TPI + sub < valid) ? d * scale_log2 : -INFINITY;
-        mx = fmaxf(mx, p[h][it]);
+        s[it] = (it * TPI + sub < valid) ? d * scale_log2 : -INFINITY;
+        mx = fmaxf(mx, s[it]);
       }
-      // online softmax: the chunk's row 0 is valid, so m_new is finite
-      const float m_new = fmaxf(m[h], sub_max<SUB>(mx));
-      const float alpha = __builtin_amdgcn_exp2f(m[h] - m_new);
-      m[h] = m_new;
-      float sum = 0.f;
+      // the chunk's row 0 is valid, so its max is finite
+      mx = sub_max<SUB>(mx);
+      if (__builtin_amdgcn_ballot_w64(mx > m[h] + kRescaleSlack)) {  // wavefront-uniform
+        const float m_new = fmaxf(m[h], mx);
+        const float alpha = __builtin_amdgcn_exp2f(m[h] - m_new);
+        m[h] = m_new;
+        l[h] *= alpha;
 #pragma unroll
-      for (int it = 0; it < VIT; ++it) {
-        p[h][it] = __builtin_amdgcn_exp2f(p[h][it] - m_new);
-        sum += p[h][it];
+        for (int e = 0; e < 8; ++e) o[h][e] *= alpha;
       }
-      l[h] = l[h] * alpha + sum;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[h][e] *= alpha;
+      for (int t2 = 0; t2 < VIT / 2; ++t2) {
+        pk[h][t2] = {static_cast<__bf16>(__builtin_amdgcn_exp2f(s[2 * t2] - m[h])),
+                     static_cast<__bf16>(__builtin_amdgcn_exp2f(s[2 * t2 + 1] - m[h]))};
+        l[h] = __builtin_amdgcn_fdot2_f32_bf16(pk[h][t2], kPairOnes, l[h], false);
+      }
     }
-    // P.V: this lane's rows' V pieces, weighted, into every head's output
+    // P.V: element pairs (token it, token it+1) of each 32-bit word of V, by byte
+    // permutes, against (p_it, p_it+1) of every head
 #pragma unroll
-    for (int it = 0; it < VIT; ++it) {
-      float v[8];
+    for (int t2 = 0; t2 < VIT / 2; ++t2) {
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        v[2 * w] = bf16_lo(buf.v[it][w]);
-        v[2 * w + 1] = bf16_hi(buf.v[it][w]);
+        const uint32_t a = buf.v[2 * t2][w], b = buf.v[2 * t2 + 1][w];
+        const bf16x2_t lo = __builtin_bit_cast(bf16x2_t, __builtin_amdgcn_perm(b, a, 0x05040100u));
+        const bf16x2_t hi = __builtin_bit_cast(bf16x2_t, __builtin_amdgcn_perm(b, a, 0x07060302u));
+#pragma unroll
+        for (int h = 0; h < GP; ++h) {
+          o[h][2 * w] = __builtin_amdgcn_fdot2_f32_bf16(lo, pk[h][t2], o[h][2 * w], false);
+          o[h][2 * w + 1] = __builtin_amdgcn_fdot2_f32_bf16(hi, pk[h][t2], o[h][2 * w + 1], false);
+        }
       }
-#pragma unroll
-      for (int h = 0; h < GP; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[h][e] += p[h][it] * v[e];
     }
   };
 
