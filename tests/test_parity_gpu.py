@@ -169,6 +169,50 @@ def test_decode_large_batch_short_contexts(pkv):
     _check_outputs(wl, _step(wl), oracle.run_step(wl))
 
 
+def _score_ramps(wl, q_amp=16.0):
+    """Give every sequence of a decode workload a designed score profile over its
+    context: dimension 0 of every query row is q_amp and dimension 0 of key t is g(t),
+    the other dimensions keep their N(0, 1) values.  Sequence i % 4 takes a rising ramp
+    (the running max climbs a fraction of a unit per token, hundreds in all), a falling
+    ramp (the first tokens dominate), a sawtooth, or flat scores with spikes of growing
+    height at a few positions."""
+    enc = workloads.round_to_bf16_bits
+    for i, s in enumerate(wl.seqs):
+        L = s.context_len
+        t = np.arange(L, dtype=np.float32)
+        kind = i % 4
+        if kind == 0:
+            g = 0.05 * t
+        elif kind == 1:
+            g = 0.05 * (L - 1 - t)
+        elif kind == 2:
+            g = 0.1 * (t % 300)
+        else:
+            g = np.zeros(L, np.float32)
+            for pos, h in ((L // 9, 30.0), (L // 3, 60.0), (L - 2, 90.0)):
+                g[pos] = h
+        k = oracle.bf16_bits_to_float(wl.k[i])
+        k[:, :, 0] = g[:, None]
+        wl.k[i][:] = enc(k)
+        q = oracle.bf16_bits_to_float(wl.q[i])
+        q[:, :, 0] = q_amp
+        wl.q[i][:] = enc(q)
+
+
+@pytest.mark.parametrize("heads", [(32, 8), (8, 8)])
+def test_decode_score_ramps(pkv, heads):
+    """Decode where the running max moves a little on most chunks and by a lot on a
+    few (and not at all after the first chunk for falling scores): the reference max
+    the kernel keeps may lag the true one by up to 2^8 before it moves."""
+    hq, hkv = heads
+    rng = np.random.default_rng(41)
+    S = workloads.SeqSpec
+    seqs = [S("decode", int(L), 1) for L in rng.integers(700, 2600, 8)]
+    wl = workloads.custom(f"ramps_{hq}_{hkv}", "bf16", hq, hkv, 128, 256, seqs, seed=41)
+    _score_ramps(wl)
+    _check_outputs(wl, _step(wl), oracle.run_step(wl))
+
+
 @pytest.mark.parametrize("case", ["bs16_gqa2", "bs256_kv8"])
 def test_prefill_many_sequences(pkv, case):
     """Prefill batches of 300 short ragged prompts (empty ones, suffix-only ones over a
