@@ -33,9 +33,12 @@
 //     head reuses each K row loaded;
 //   * online softmax in the log2 domain (scale * log2 e folded into one multiply):
 //     max over the chunk's rows in-lane and, across the rows one instruction spreads
-//     over lanes, with v_permlane16/32_swap; exp2; per-lane shares of the row sum;
-//   * P.V: each lane accumulates its rows' weighted V pieces; the lanes holding one
-//     head_dim piece of a head are summed once, at the end of the segment.
+//     over lanes, with v_permlane16/32_swap; the reference max moves only when a chunk
+//     exceeds it by more than 2^8; exp2, rounded to bf16; per-lane shares of the row
+//     sum of those rounded values;
+//   * P.V: each lane accumulates its rows' weighted V pieces as bf16 pair dot products
+//     over two of its rows (fp32 accumulation); the lanes holding one head_dim piece of
+//     a head are summed once, at the end of the segment.
 // q changes only with the stream, so it is loaded once per segment.
 // Rows past context_len are never read: the buffer loads' range check returns zeros
 // for them (block_size >= CH), or they re-read the chunk's last valid row (smaller
