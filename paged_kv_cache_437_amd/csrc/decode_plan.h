@@ -21,12 +21,16 @@ constexpr int kMaxAutoWorkers = 4096;  // bound on the automatic worker count
 inline int heads_per_stream(int G) { return G >= 8 ? 8 : (G >= 4 ? 4 : (G >= 2 ? 2 : 1)); }
 
 // kv heads per stream: the largest power of two that divides Hkv and spans at most
-// 512 contiguous bytes of a token's row (2 at head_dim 128, 4 at 64).  Measured on
-// the decode: 512 bytes per token beat 256 and 1 KB (whose 4-token chunks cost more
-// per byte).
-inline int kv_heads_per_stream(int D, int Hkv) {
+// 512 contiguous bytes of a token's row (2 at head_dim 128, 4 at 64), or 1 KB from 8 q
+// heads per kv head up.  Measured on the decode at head_dim 128: with one q head per
+// kv head 512 bytes per token beat 256 and 1 KB (whose 4-token chunks cost more per
+// byte; 1 KB was 8% slower); at 4 q heads per kv head 512 bytes and 1 KB tie; at 8,
+// 1 KB is 8% faster (the wider stream halves the streams, each chunk's vector work
+// being the same).
+inline int kv_heads_per_stream(int D, int Hkv, int G) {
+  const int limit = heads_per_stream(G) >= 8 ? 1024 : 512;
   int mh = 1;
-  while (mh * 2 * D * 2 <= 512 && Hkv % (mh * 2) == 0) mh *= 2;
+  while (mh * 2 * D * 2 <= limit && Hkv % (mh * 2) == 0) mh *= 2;
   return mh;
 }
 

@@ -44,7 +44,7 @@ hipError_t launch_mixed_attention_bf16(
     int max_position, hipStream_t stream) {
   const int G = num_q_heads / num_kv_heads;
   const int GP = heads_per_stream(G);
-  const int MH = kv_heads_per_stream(head_dim, num_kv_heads);
+  const int MH = kv_heads_per_stream(head_dim, num_kv_heads, G);
   // the shapes built here: both passes take their whole-block paths and one grouping
   if (G > 8 || bs_log2 < 6 || (1 << bs_log2) < chunk_tokens(head_dim, MH) || prefill_batch <= 0 ||
       decode_batch <= 0 || max_seqlen_q <= 0)

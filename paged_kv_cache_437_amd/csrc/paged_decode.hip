@@ -127,7 +127,7 @@ hipError_t launch_decode_gp(int GP, const void* q, void* out, const void* k_cach
 
 int paged_decode_bf16_workers(int head_dim, int num_q_heads, int num_kv_heads, int bs_log2) {
   const int GP = heads_per_stream(num_q_heads / num_kv_heads);
-  const int MH = kv_heads_per_stream(head_dim, num_kv_heads);
+  const int MH = kv_heads_per_stream(head_dim, num_kv_heads, num_q_heads / num_kv_heads);
   const bool one = (1 << bs_log2) >= chunk_tokens(head_dim, MH);
 #define PKV_W(D_, GP_, MH_)                                                   \
   if (head_dim == D_ && GP == GP_ && MH == MH_)                               \
@@ -143,7 +143,7 @@ int paged_decode_bf16_workers(int head_dim, int num_q_heads, int num_kv_heads, i
 size_t paged_decode_bf16_workspace(int head_dim, int num_q_heads, int num_kv_heads, int batch,
                                    int num_workers) {
   const int GP = heads_per_stream(num_q_heads / num_kv_heads);
-  const int MH = kv_heads_per_stream(head_dim, num_kv_heads);
+  const int MH = kv_heads_per_stream(head_dim, num_kv_heads, num_q_heads / num_kv_heads);
   return decode_workspace_bytes(batch, num_workers > 0 ? num_workers : kMaxAutoWorkers, MH * GP,
                                 head_dim);
 }
@@ -155,7 +155,7 @@ hipError_t launch_paged_decode_bf16(int head_dim, const void* q, void* out, cons
                                     int num_workers, void* workspace, const float* cos_sin,
                                     int max_position, hipStream_t stream) {
   const int GP = heads_per_stream(num_q_heads / num_kv_heads);
-  const int MH = kv_heads_per_stream(head_dim, num_kv_heads);
+  const int MH = kv_heads_per_stream(head_dim, num_kv_heads, num_q_heads / num_kv_heads);
 #define PKV_DEC(D_, MH_)                                                                      \
   return launch_decode_gp<D_, MH_>(GP, q, out, k_cache, v_cache, num_q_heads, num_kv_heads, \
                                    bs_log2, batch, context_lens, block_tables, table_stride, \
