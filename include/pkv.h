@@ -171,7 +171,7 @@ size_t pkv_paged_decode_workspace_size(const pkv_cache* cache, int32_t num_q_hea
  *                   tokens, and the list of all chunks is divided evenly among this
  *                   many wavefront workers; a stream cut between workers is merged
  *                   exactly (log-sum-exp) by a second kernel.  0 = one worker per
- *                   SIMD for GP <= 2 and two for larger GP (at most 4096); W in
+ *                   SIMD for GP <= 4 and two for larger GP (at most 4096); W in
  *                   [1, 2^20] = exactly W (1 = no cut at all).  Ignored by the fp32
  *                   path, which never cuts.
  * The cut depends only on lengths and the worker count, never on block ids, so
