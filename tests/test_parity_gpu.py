@@ -213,6 +213,23 @@ def test_decode_score_ramps(pkv, heads):
     _check_outputs(wl, _step(wl), oracle.run_step(wl))
 
 
+@pytest.mark.parametrize("heads", [(16, 8), (32, 8)])
+def test_prefill_score_ramps(pkv, heads):
+    """Prefill (whole prompts and suffixes over a stored prefix) with the same designed
+    score profiles: every query row's reference max lags or jumps as the keys it sees
+    rise, fall, saw or spike."""
+    hq, hkv = heads
+    rng = np.random.default_rng(43)
+    S = workloads.SeqSpec
+    seqs = []
+    for k in range(8):
+        L = int(rng.integers(300, 1500))
+        seqs.append(S("prefill", L, L if k % 2 == 0 else int(rng.integers(1, L // 2))))
+    wl = workloads.custom(f"pf_ramps_{hq}_{hkv}", "bf16", hq, hkv, 128, 256, seqs, seed=43)
+    _score_ramps(wl)
+    _check_outputs(wl, _step(wl), oracle.run_step(wl))
+
+
 @pytest.mark.parametrize("case", ["bs16_gqa2", "bs256_kv8"])
 def test_prefill_many_sequences(pkv, case):
     """Prefill batches of 300 short ragged prompts (empty ones, suffix-only ones over a
