@@ -9,7 +9,10 @@
 
 namespace pkv {
 
-template <int D, int GP, int MH, bool ROT>
+// GP: the decode pass's q heads per stream (G rounded down to a power of two, the
+// rest in further streams); PGP: the prefill pass's q heads per work item, which must
+// cover all G of a kv head (G rounded up to a power of two).
+template <int D, int GP, int PGP, int MH, bool ROT>
 __global__ __launch_bounds__(256, 2) void mixed_attention_bf16_kernel(
     const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache, int Hq, int Hkv,
     int G, int bs_log2, float scale_log2, const float* __restrict__ cos_sin, int max_position,
@@ -29,7 +32,7 @@ __global__ __launch_bounds__(256, 2) void mixed_attention_bf16_kernel(
                                            bs_log2, scale_log2, num_workers, ws_prefix, ws_ml,
                                            ws_o, cos_sin, max_position);
   else
-    prefill_workgroup<D, GP, true, ROT>(blockIdx.x - n_decode_wg, pq, pout, k_cache, v_cache,
+    prefill_workgroup<D, PGP, true, ROT>(blockIdx.x - n_decode_wg, pq, pout, k_cache, v_cache,
                                         cu_q, cu_k, p_tables, p_stride, Hq, Hkv, G, bs_log2,
                                         scale_log2, p_batch, max_tiles, cos_sin, max_position);
 }
@@ -44,6 +47,7 @@ hipError_t launch_mixed_attention_bf16(
     int max_position, hipStream_t stream) {
   const int G = num_q_heads / num_kv_heads;
   const int GP = heads_per_stream(G);
+  const int PGP = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8;  // as the prefill kernel rounds
   const int MH = kv_heads_per_stream(head_dim, num_kv_heads, G);
   // the shapes built here: both passes take their whole-block paths and one grouping
   if (G > 8 || bs_log2 < 6 || (1 << bs_log2) < chunk_tokens(head_dim, MH) || prefill_batch <= 0 ||
@@ -58,14 +62,14 @@ hipError_t launch_mixed_attention_bf16(
   // a multiple of 8 (the surplus workgroups have no worker and leave at once), so the
   // prefill's item w sits on the XCD that w mod 8 names
   const int n_decode_wg = ((W + 3) / 4 + kXcds - 1) / kXcds * kXcds;
-  const int bm_tok = 128 / GP;
+  const int bm_tok = 128 / PGP;
   const int max_tiles = (max_seqlen_q + bm_tok - 1) / bm_tok;
   const int64_t slots = static_cast<int64_t>(prefill_batch) * num_kv_heads * max_tiles;
   if (slots + n_decode_wg > 0x7fffffff) return hipErrorInvalidConfiguration;
   const dim3 grid(static_cast<unsigned>(slots + n_decode_wg));
   const float scale_log2 = scale * kLog2e;
-#define PKV_MIXED(D_, GP_, MH_, ROT_)                                                          \
-  hipLaunchKernelGGL((mixed_attention_bf16_kernel<D_, GP_, MH_, ROT_>), grid, dim3(256), 0,     \
+#define PKV_MIXED(D_, GP_, PGP_, MH_, ROT_)                                                    \
+  hipLaunchKernelGGL((mixed_attention_bf16_kernel<D_, GP_, PGP_, MH_, ROT_>), grid, dim3(256), 0, \
                      stream, static_cast<const uint16_t*>(k_cache),                           \
                      static_cast<const uint16_t*>(v_cache), num_q_heads, num_kv_heads, G,     \
                      bs_log2, scale_log2, cos_sin, max_position, n_decode_wg,                 \
@@ -74,16 +78,18 @@ hipError_t launch_mixed_attention_bf16(
                      ws.prefix, ws.ml, ws.o, static_cast<const uint16_t*>(q_prefill),         \
                      static_cast<uint16_t*>(out_prefill), cu_seqlens_q, cu_seqlens_k,         \
                      prefill_tables, prefill_stride, prefill_batch, max_tiles)
-#define PKV_MIXED_R(D_, GP_, MH_)                   \
-  if (cos_sin != nullptr) PKV_MIXED(D_, GP_, MH_, true); \
-  else PKV_MIXED(D_, GP_, MH_, false);
-#define PKV_MIXED_GP(D_, MH_)                       \
-  switch (GP) {                                     \
-    case 1: PKV_MIXED_R(D_, 1, MH_) break;          \
-    case 2: PKV_MIXED_R(D_, 2, MH_) break;          \
-    case 4: PKV_MIXED_R(D_, 4, MH_) break;          \
-    default: PKV_MIXED_R(D_, 8, MH_) break;         \
-  }
+#define PKV_MIXED_R(D_, GP_, PGP_, MH_)                   \
+  if (cos_sin != nullptr) PKV_MIXED(D_, GP_, PGP_, MH_, true); \
+  else PKV_MIXED(D_, GP_, PGP_, MH_, false);
+  // (GP, PGP) pairs: G = 1 -> (1, 1), 2 -> (2, 2), 3 -> (2, 4), 4 -> (4, 4),
+  // 5..7 -> (4, 8), 8 -> (8, 8)
+#define PKV_MIXED_GP(D_, MH_)                                        \
+  if (GP == 1) { PKV_MIXED_R(D_, 1, 1, MH_) }                        \
+  else if (GP == 2 && PGP == 2) { PKV_MIXED_R(D_, 2, 2, MH_) }       \
+  else if (GP == 2) { PKV_MIXED_R(D_, 2, 4, MH_) }                   \
+  else if (GP == 4 && PGP == 4) { PKV_MIXED_R(D_, 4, 4, MH_) }       \
+  else if (GP == 4) { PKV_MIXED_R(D_, 4, 8, MH_) }                   \
+  else { PKV_MIXED_R(D_, 8, 8, MH_) }
   timing_begin("mixed_attention", stream);
   if (head_dim == 128) {
     switch (MH) {

@@ -31,6 +31,16 @@ def _cases():
         ("one launch, GQA 8", workloads.custom(
             "mixed_g8_d128_bs256", "bf16", 16, 2, 128, 256,
             [S("prefill", 257, 257), S("decode", 1000, 1), S("decode", 17, 1)], seed=33), True),
+        # 3 and 7 q heads per kv head: the decode's streams hold 2 and 4 of them (the
+        # rest in a second stream) while each prefill item must hold all of them
+        ("one launch, GQA 3", workloads.custom(
+            "mixed_g3_d128_bs256", "bf16", 12, 4, 128, 256,
+            [S("prefill", 300, 300), S("decode", 700, 1), S("prefill", 900, 129),
+             S("decode", 5, 1)], seed=36), True),
+        ("one launch, GQA 7, D64", workloads.custom(
+            "mixed_g7_d64_bs128", "bf16", 14, 2, 64, 128,
+            [S("decode", 1000, 1), S("prefill", 200, 200), S("decode", 129, 1),
+             S("prefill", 40, 17)], seed=37), True),
         ("two passes: fp32", workloads.tiny_mixed(seed=0), False),
         ("two passes: block 16", workloads.custom(
             "mixed_bs16", "bf16", 8, 2, 128, 16,
@@ -45,7 +55,7 @@ def _bits(a):
     return a.view(np.uint64)
 
 
-@pytest.mark.parametrize("idx", range(6))
+@pytest.mark.parametrize("idx", range(8))
 @pytest.mark.parametrize("rot", [False, True])
 def test_mixed_matches_separate_calls(idx, rot):
     import paged_kv_cache_437_amd as pkv
