@@ -149,26 +149,22 @@ __device__ __forceinline__ int swz(int r) {
 typedef __attribute__((address_space(3))) char lds_char;
 
 // 16 bytes per lane from global memory straight into LDS: lane l's 16 bytes land at
-// LDS byte lds + 16 l.  Issued as inline assembly so the compiler does not track it:
-// the kernel orders these writes against the LDS reads itself (vmcnt(0) and a
-// barrier before a tile is read; a buffer is refilled only after every wave is done
-// with it).  The load takes its LDS address in m0, set in the same statement; in the
-// compiled prefill and mixed-step kernels no other instruction reads or writes m0, so
-// the clobber (which the compiler warns it may not preserve) loses nothing.
+// LDS byte lds + 16 l (global_load_lds_dwordx4; the compiler sets the LDS base in m0
+// itself).  Each wave orders these writes against the other waves' LDS reads
+// explicitly: vmcnt(0) and a barrier before a tile is read, and a buffer is refilled
+// only after every wave is done with it.
+typedef __attribute__((address_space(1))) const void global_cvoid;
+typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ uint32_t lds_addr(const char* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_char*)p));
 }
 __device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :
-               : "s"(lds), "v"(voff), "s"(sbase)
-               : "memory", "m0");
+  __builtin_amdgcn_global_load_lds((global_cvoid*)(sbase + voff),
+                                   (lds_void*)static_cast<uintptr_t>(lds), 16, 0, 0);
 }
 __device__ __forceinline__ void dma16_ptr(const void* p, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :
-               : "s"(lds), "v"(p)
-               : "memory", "m0");
+  __builtin_amdgcn_global_load_lds((global_cvoid*)p, (lds_void*)static_cast<uintptr_t>(lds), 16,
+                                   0, 0);
 }
 
 // One workgroup (one work item of the list) of the prefill pass; the kernels that run
