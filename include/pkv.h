@@ -16,8 +16,10 @@
  *  - Every array pointer of the data-plane calls (store, prefill, decode) is a
  *    DEVICE pointer owned by the caller.  The library allocates no device memory,
  *    keeps no state between calls, never synchronises, and enqueues all its work
- *    on `stream`.  Calls are reentrant.  The block manager (pkv_bm_*) is host-only
- *    and takes host arrays.
+ *    on `stream`.  Calls are reentrant.  (Exceptions, each said where it is
+ *    declared: the contract checks and debug mode synchronise and report through a
+ *    status word the library holds per device.)  The block manager (pkv_bm_*) is
+ *    host-only and takes host arrays.
  *  - Element type: q, k, v, both caches and out share one type (pkv_dtype).
  *    Metadata arrays are int32.
  *  - Cache layout (one layer): k_cache and v_cache are each
@@ -29,7 +31,8 @@
  *    at position Lk - Lq + i; it sees keys 0 .. Lk - Lq + i.
  *  - Host scalars are validated before any HIP call; a bad one returns an error
  *    status and touches nothing.  Device arrays are the caller's contract and
- *    are not read on the host (see each call).  Results never depend on cache
+ *    are not read on the host (see each call); pkv_validate_* and debug mode
+ *    (PKV_DEBUG) check them.  Results never depend on cache
  *    rows outside a sequence's (table, length): stale or NaN contents of freed
  *    blocks and of the unused tail of a sequence's last block cannot leak.
  *  - Supported: head_dim 64 or 128; block_size a power of two in [1, 256];
@@ -147,11 +150,13 @@ pkv_status pkv_paged_prefill_rotary(const pkv_cache* cache, const void* q, void*
 /* Bytes of device workspace pkv_paged_decode needs for this shape; num_workers as
  * in pkv_paged_decode.  0 for the fp32 path (it needs none) and for invalid
  * arguments.  For bf16: 2*W*HS*(4*head_dim + 8) + 8*(batch + 1) bytes, rounded up
- * to 256-byte pieces, with W = num_workers (4096 when 0) and HS = MH*GP heads per
- * stream (see num_workers): GP = q heads per kv head rounded up to a power of two,
- * at most 8; MH = the largest power of two dividing num_kv_heads with
- * MH*head_dim*2 <= 512 (about 8.6 MB at head_dim 128, 32 q / 32 kv heads and
- * W = 4096).  max_context_len does not change it. */
+ * to 256-byte pieces, with W = num_workers (the automatic count when 0) and HS =
+ * MH*GP heads per stream (see num_workers): GP = q heads per kv head rounded down to
+ * a power of two, at most 8; MH = the largest power of two dividing num_kv_heads with
+ * MH*head_dim*2 <= 512 bytes (1024 from GP 8 up) (about 2.1 MB at head_dim 128, 32 q /
+ * 32 kv heads and the automatic W = 1024).  max_context_len does not change it.  The
+ * worker count is an argument, unlike the survey's four-argument form, because the
+ * workspace scales with it and a caller may choose it. */
 size_t pkv_paged_decode_workspace_size(const pkv_cache* cache, int32_t num_q_heads,
                                        int32_t batch, int32_t max_context_len,
                                        int32_t num_workers);
@@ -170,12 +175,13 @@ size_t pkv_paged_decode_workspace_size(const pkv_cache* cache, int32_t num_q_hea
  *                   heads of each); its K/V is cut into chunks of 2048/(head_dim*MH)
  *                   tokens, and the list of all chunks is divided evenly among this
  *                   many wavefront workers; a stream cut between workers is merged
- *                   exactly (log-sum-exp) by a second kernel.  0 = one worker per
- *                   SIMD for GP <= 4 and two for larger GP (at most 4096); W in
- *                   [1, 2^20] = exactly W (1 = no cut at all).  Ignored by the fp32
- *                   path, which never cuts.
- * The cut depends only on lengths and the worker count, never on block ids, so
- * results are bit-identical under any relabelling of physical blocks. */
+ *                   exactly (log-sum-exp) by a second kernel.  0 = automatic:
+ *                   1024 workers while GP <= 4, 2048 for GP 8 (a constant of the
+ *                   shape, never read from the device); W in [1, 2^20] = exactly W
+ *                   (1 = no cut at all).  Ignored by the fp32 path, which never cuts.
+ * Where a context is cut depends only on the lengths, the shape and the worker count,
+ * never on block ids or on the device, so results are bit-identical under any
+ * relabelling of physical blocks and on any part. */
 pkv_status pkv_paged_decode(const pkv_cache* cache, const void* q, void* out,
                             int32_t num_q_heads, int32_t batch,
                             const int32_t* context_lens, int32_t max_context_len,
@@ -293,6 +299,63 @@ pkv_status pkv_bm_deallocate(pkv_block_manager* bm, int64_t seq);
  * capacity 0 to ask for the length. */
 int32_t pkv_bm_block_table(const pkv_block_manager* bm, int64_t seq, int32_t* out,
                            int32_t capacity);
+
+/* ---- Contract checks of the metadata arrays (a debugging aid).
+ * The data-plane calls trust their device arrays: block ids and slots are chosen on the
+ * host by the control plane and the GPU only copies into and reads from them
+ * (“深入 Nano-vLLM 推理引擎”, "Control plane vs. data plane"), so a bad slot or length would
+ * become an access outside the pool.  These calls check the arrays one data-plane call
+ * would read against its contract and report each kind of violation found as a bit:
+ *   PKV_BAD_SLOT     a slot outside [0, num_blocks*block_size) other than -1
+ *   PKV_DUP_SLOT     a valid slot that appears twice in one call (a write race)
+ *   PKV_BAD_TABLE    a used block-table entry (entries 0 .. ceil(L/block_size)-1 of a
+ *                    row, capped at the stride) outside [0, num_blocks)
+ *   PKV_BAD_SEQLENS  cu_seqlens_q[0] or cu_seqlens_k[0] not 0, a negative length, Lk <
+ *                    Lq, Lk = 0 with Lq > 0, Lq > max_seqlen_q or Lk > max_seqlen_k
+ *   PKV_BAD_CONTEXT  a context length < 1 or > max_context_len
+ *   PKV_BAD_STRIDE   ceil(L/block_size) > block_table_stride
+ * arrays_on_host != 0: the arrays are host arrays, checked on the calling thread (stream
+ * unused).  arrays_on_host == 0: they are device arrays, checked by a kernel on `stream`
+ * that reports through a status word the library holds per device (no allocation); the
+ * call then waits for the stream.  Two device checks in flight on one device at once
+ * share that word and race.  Every read stays inside the sizes passed (num_tokens,
+ * batch + 1 cumulative lengths, batch rows of block_table_stride entries), whatever
+ * the arrays hold.  Returns PKV_OK when every contract holds, PKV_ERR_INVALID (with
+ * pkv_last_error naming the violations) when one does not, another status if the check
+ * itself could not run; *violations (may be NULL) receives the bits.
+ * Debug mode: while pkv_debug_enabled() is 1 (initially when the environment variable
+ * PKV_DEBUG is set and not "0"), every data-plane call first checks its device arrays
+ * this way and returns the violation without launching anything. */
+typedef enum {
+  PKV_BAD_SLOT = 1,
+  PKV_DUP_SLOT = 2,
+  PKV_BAD_TABLE = 4,
+  PKV_BAD_SEQLENS = 8,
+  PKV_BAD_CONTEXT = 16,
+  PKV_BAD_STRIDE = 32
+} pkv_contract;
+
+/* Arrays of pkv_store_kvcache (only num_blocks and block_size of `cache` are used). */
+pkv_status pkv_validate_store(const pkv_cache* cache, const int32_t* slot_mapping,
+                              int32_t num_tokens, int32_t arrays_on_host, uint32_t* violations,
+                              hipStream_t stream);
+/* Arrays of pkv_paged_prefill. */
+pkv_status pkv_validate_prefill(const pkv_cache* cache, int32_t batch,
+                                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                const int32_t* block_tables, int32_t block_table_stride,
+                                int32_t arrays_on_host, uint32_t* violations,
+                                hipStream_t stream);
+/* Arrays of pkv_paged_decode. */
+pkv_status pkv_validate_decode(const pkv_cache* cache, int32_t batch,
+                               const int32_t* context_lens, int32_t max_context_len,
+                               const int32_t* block_tables, int32_t block_table_stride,
+                               int32_t arrays_on_host, uint32_t* violations,
+                               hipStream_t stream);
+/* Turns debug mode on (on != 0) or off for the whole process. */
+pkv_status pkv_debug_enable(int32_t on);
+/* 1 while debug mode is on, else 0. */
+int32_t pkv_debug_enabled(void);
 
 /* Kernel timing, off by default (tracing support for benchmarks).  While on,
  * every kernel the library launches is bracketed by two hipEvents recorded on

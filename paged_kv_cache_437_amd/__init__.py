@@ -30,7 +30,8 @@ from ._lib import PkvError
 
 __all__ = ["store_kvcache", "paged_prefill", "paged_decode", "paged_decode_workspace_size",
            "mixed_attention", "rotary_table", "PkvError", "version", "library_path", "timing_enable",
-           "timing_collect"]
+           "timing_collect", "validate_store", "validate_prefill", "validate_decode",
+           "contract_names", "debug_enable", "debug_enabled"]
 
 _DTYPES = {torch.float32: _lib.PKV_F32, torch.bfloat16: _lib.PKV_BF16}
 
@@ -252,3 +253,95 @@ def mixed_attention(k_cache: torch.Tensor, v_cache: torch.Tensor, scale: float,
         decode_tables.shape[1] if decode_tables.dim() == 2 else 0, ws_ptr, ws_bytes,
         int(num_workers), None if rot is None else ctypes.byref(rot), _stream(k_cache.device)))
     return out_prefill, out_decode
+
+
+# ---- contract checks of the metadata arrays (the library's pkv_validate_*) ----
+
+def _meta(a, name: str):
+    """(pointer, on_host, keepalive) of an int32 metadata array: a numpy array or CPU
+    tensor is checked on the host, a device tensor on its device."""
+    import numpy as np
+    if isinstance(a, torch.Tensor):
+        if a.dtype != torch.int32:
+            raise ValueError(f"{name} must be int32, got {a.dtype}")
+        a = a.contiguous()
+        return a.data_ptr(), (not a.is_cuda), a
+    arr = np.ascontiguousarray(a, dtype=np.int32)
+    return arr.ctypes.data, True, arr
+
+
+def _meta_desc(num_blocks: int, block_size: int) -> _lib.PkvCache:
+    return _lib.PkvCache(None, None, int(num_blocks), int(block_size), 1, 128, _lib.PKV_BF16)
+
+
+def _run_check(fn, device_arrays, *args) -> int:
+    bits = ctypes.c_uint32(0)
+    stream = None
+    for t in device_arrays:
+        if isinstance(t, torch.Tensor) and t.is_cuda:
+            stream = _stream(t.device)
+    st = fn(*args, ctypes.byref(bits), stream)
+    if st not in (_lib.PKV_OK, _lib.PKV_ERR_INVALID) or (st == _lib.PKV_ERR_INVALID and
+                                                         bits.value == 0):
+        _lib.check(st)
+    return int(bits.value)
+
+
+def validate_store(slot_mapping, num_blocks: int, block_size: int) -> int:
+    """Contract bits (0 = every contract holds) of a KV write's slot mapping: slots in
+    [0, num_blocks*block_size) or -1, no valid slot twice."""
+    lib = _lib.load()
+    ptr, host, keep = _meta(slot_mapping, "slot_mapping")
+    n = keep.numel() if isinstance(keep, torch.Tensor) else keep.size
+    return _run_check(lib.pkv_validate_store, [slot_mapping],
+                      ctypes.byref(_meta_desc(num_blocks, block_size)), ptr, n, int(host))
+
+
+def validate_prefill(cu_seqlens_q, cu_seqlens_k, block_tables, max_seqlen_q: int,
+                     max_seqlen_k: int, num_blocks: int, block_size: int) -> int:
+    """Contract bits of a prefill's cumulative lengths and block tables."""
+    lib = _lib.load()
+    pq, hq, kq = _meta(cu_seqlens_q, "cu_seqlens_q")
+    pk, hk, kk = _meta(cu_seqlens_k, "cu_seqlens_k")
+    pt, ht, kt = _meta(block_tables, "block_tables")
+    if not (hq == hk == ht):
+        raise ValueError("metadata arrays must all be on the host or all on the device")
+    batch = (kq.numel() if isinstance(kq, torch.Tensor) else kq.size) - 1
+    stride = kt.shape[1] if kt.ndim == 2 else 0
+    if kt.shape[0] != batch or (kk.numel() if isinstance(kk, torch.Tensor) else kk.size) != batch + 1:
+        raise ValueError("cu_seqlens_q, cu_seqlens_k and block_tables disagree on batch")
+    return _run_check(lib.pkv_validate_prefill, [cu_seqlens_q],
+                      ctypes.byref(_meta_desc(num_blocks, block_size)), batch, pq, pk,
+                      int(max_seqlen_q), int(max_seqlen_k), pt, stride, int(hq))
+
+
+def validate_decode(context_lens, block_tables, max_context_len: int, num_blocks: int,
+                    block_size: int) -> int:
+    """Contract bits of a decode's context lengths and block tables."""
+    lib = _lib.load()
+    pc, hc, kc = _meta(context_lens, "context_lens")
+    pt, ht, kt = _meta(block_tables, "block_tables")
+    if hc != ht:
+        raise ValueError("metadata arrays must all be on the host or all on the device")
+    batch = kc.numel() if isinstance(kc, torch.Tensor) else kc.size
+    stride = kt.shape[1] if kt.ndim == 2 else 0
+    if kt.shape[0] != batch:
+        raise ValueError("context_lens and block_tables disagree on batch")
+    return _run_check(lib.pkv_validate_decode, [context_lens],
+                      ctypes.byref(_meta_desc(num_blocks, block_size)), batch, pc,
+                      int(max_context_len), pt, stride, int(hc))
+
+
+def contract_names(bits: int) -> list:
+    """The violated contracts a validate_* result names."""
+    return [v for k, v in _lib.CONTRACTS.items() if bits & k]
+
+
+def debug_enable(on: bool = True) -> None:
+    """Debug mode: every data-plane call checks its device metadata first and fails with
+    PkvError instead of launching (initially on when PKV_DEBUG is set and not "0")."""
+    _lib.check(_lib.load().pkv_debug_enable(1 if on else 0))
+
+
+def debug_enabled() -> bool:
+    return bool(_lib.load().pkv_debug_enabled())

@@ -25,7 +25,20 @@ EXPORTED = (
     "pkv_bm_add_sequence", "pkv_bm_remove_sequence", "pkv_bm_can_allocate", "pkv_bm_allocate",
     "pkv_bm_num_cached_tokens", "pkv_bm_num_tokens", "pkv_bm_can_append",
     "pkv_bm_append_token", "pkv_bm_deallocate", "pkv_bm_block_table",
+    "pkv_validate_store", "pkv_validate_prefill", "pkv_validate_decode", "pkv_debug_enable",
+    "pkv_debug_enabled",
 )
+
+# contract bits of pkv_validate_* (include/pkv.h)
+CONTRACTS = {
+    1: "slot outside [0, num_blocks*block_size) and not -1",
+    2: "a slot written twice in one call",
+    4: "a used block-table entry outside [0, num_blocks)",
+    8: "cu_seqlens not from 0 / negative length, Lk < Lq, Lk = 0 with Lq > 0, or a length "
+       "above its max",
+    16: "a context length < 1 or above max_context_len",
+    32: "ceil(length / block_size) > block_table_stride",
+}
 
 
 class PkvCache(ctypes.Structure):
@@ -124,6 +137,17 @@ def load() -> ctypes.CDLL:
         getattr(lib, name).restype = I
     lib.pkv_bm_destroy.argtypes = [P]
     lib.pkv_bm_destroy.restype = None
+    U32P = ctypes.POINTER(ctypes.c_uint32)
+    lib.pkv_validate_store.argtypes = [cache_p, P, I, I, U32P, P]
+    lib.pkv_validate_store.restype = I
+    lib.pkv_validate_prefill.argtypes = [cache_p, I, P, P, I, I, P, I, I, U32P, P]
+    lib.pkv_validate_prefill.restype = I
+    lib.pkv_validate_decode.argtypes = [cache_p, I, P, I, P, I, I, U32P, P]
+    lib.pkv_validate_decode.restype = I
+    lib.pkv_debug_enable.argtypes = [I]
+    lib.pkv_debug_enable.restype = I
+    lib.pkv_debug_enabled.argtypes = []
+    lib.pkv_debug_enabled.restype = I
     _lib = lib
     return lib
 

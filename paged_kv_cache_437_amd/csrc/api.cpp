@@ -9,6 +9,7 @@
 #include "../../include/pkv.h"
 #include "errors.h"
 #include "launch.h"
+#include "validate.h"
 
 namespace {
 
@@ -91,7 +92,7 @@ pkv_status launched(hipError_t e, const char* what) {
 
 size_t elem_size(const pkv_cache* c) { return c->dtype == PKV_F32 ? 4 : 2; }
 
-// upper bound on an explicit decode worker count (the automatic count is at most 4096)
+// upper bound on an explicit decode worker count (the automatic count is 1024 or 2048)
 constexpr int32_t kMaxWorkers = 1 << 20;
 
 }  // namespace
@@ -125,6 +126,9 @@ pkv_status pkv_store_kvcache_rotary(const pkv_cache* cache, const void* k, const
   if (num_tokens == 0) return ok();
   if (k == nullptr || v == nullptr || slot_mapping == nullptr || positions == nullptr)
     return fail(PKV_ERR_INVALID, "k, v, slot_mapping or positions is NULL");
+  if (pkv::debug_checks_on() &&
+      (st = pkv_validate_store(cache, slot_mapping, num_tokens, 0, nullptr, stream)) != PKV_OK)
+    return st;
   return launched(pkv::launch_store_kvcache_rotary(
                       cache->dtype == PKV_BF16, cache->head_dim, cache->k_cache, cache->v_cache,
                       k, v, slot_mapping, positions, num_tokens, cache->num_kv_heads,
@@ -143,6 +147,9 @@ pkv_status pkv_store_kvcache(const pkv_cache* cache, const void* k, const void* 
     return fail(PKV_ERR_INVALID, "k, v or slot_mapping is NULL");
   const size_t row_bytes = elem_size(cache) * cache->num_kv_heads * cache->head_dim;
   if (row_bytes > (1u << 30)) return fail(PKV_ERR_UNSUPPORTED, "row of %zu bytes", row_bytes);
+  if (pkv::debug_checks_on() &&
+      (st = pkv_validate_store(cache, slot_mapping, num_tokens, 0, nullptr, stream)) != PKV_OK)
+    return st;
   return launched(pkv::launch_store_kvcache(cache->k_cache, cache->v_cache, k, v, slot_mapping,
                                             num_tokens, static_cast<int32_t>(row_bytes), stream),
                   "store_kvcache");
@@ -175,6 +182,11 @@ pkv_status prefill_impl(const pkv_cache* cache, const void* q, void* out, int32_
   if (!(scale > 0.f) || !std::isfinite(scale))
     return fail(PKV_ERR_INVALID, "scale %g must be finite and positive", scale);
   if (dry) return PKV_OK;
+  if (pkv::debug_checks_on() &&
+      (st = pkv_validate_prefill(cache, batch, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                                 max_seqlen_k, block_tables, block_table_stride, 0, nullptr,
+                                 stream)) != PKV_OK)
+    return st;
   const int bs_log2 = log2_exact(cache->block_size);
   const float* cs = rot != nullptr ? rot->cos_sin : nullptr;
   const int max_pos = rot != nullptr ? rot->max_position : 0;
@@ -263,6 +275,10 @@ pkv_status decode_impl(const pkv_cache* cache, const void* q, void* out, int32_t
   if (ws > 0 && (workspace == nullptr || workspace_bytes < ws))
     return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, ws);
   if (dry) return PKV_OK;
+  if (pkv::debug_checks_on() &&
+      (st = pkv_validate_decode(cache, batch, context_lens, max_context_len, block_tables,
+                                block_table_stride, 0, nullptr, stream)) != PKV_OK)
+    return st;
   const int bs_log2 = log2_exact(cache->block_size);
   const float* cs = rot != nullptr ? rot->cos_sin : nullptr;
   const int max_pos = rot != nullptr ? rot->max_position : 0;
@@ -330,6 +346,14 @@ pkv_status pkv_mixed_attention(const pkv_cache* cache, int32_t num_q_heads, floa
                         workspace_bytes, num_workers, rotary, stream, true)) != PKV_OK)
     return st;
   if (cache->dtype == PKV_BF16 && prefill_batch > 0 && max_seqlen_q > 0 && decode_batch > 0) {
+    if (pkv::debug_checks_on() &&
+        ((st = pkv_validate_prefill(cache, prefill_batch, cu_seqlens_q, cu_seqlens_k,
+                                    max_seqlen_q, max_seqlen_k, prefill_tables,
+                                    prefill_table_stride, 0, nullptr, stream)) != PKV_OK ||
+         (st = pkv_validate_decode(cache, decode_batch, context_lens, max_context_len,
+                                   decode_tables, decode_table_stride, 0, nullptr, stream)) !=
+             PKV_OK))
+      return st;
     const hipError_t e = pkv::launch_mixed_attention_bf16(
         cache->head_dim, cache->k_cache, cache->v_cache, num_q_heads, cache->num_kv_heads,
         log2_exact(cache->block_size), scale, q_prefill, out_prefill, prefill_batch,

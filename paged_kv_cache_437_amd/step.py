@@ -13,11 +13,30 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (mixed_attention, paged_decode, paged_decode_workspace_size, paged_prefill,
-               store_kvcache)
+from . import (contract_names, mixed_attention, paged_decode, paged_decode_workspace_size,
+               paged_prefill, store_kvcache, validate_decode, validate_prefill, validate_store)
 from .control import BlockPool, plan_step
 
-__all__ = ["DeviceStep", "to_device_values", "STALE_BITS"]
+__all__ = ["DeviceStep", "check_plan", "to_device_values", "STALE_BITS"]
+
+
+def check_plan(plan, num_blocks: int, block_size: int) -> None:
+    """The data-plane contracts on the control plane's host copies of a step's metadata,
+    before any of it reaches the device (the library's host-side checks): slots in the
+    pool and written once per call, used table entries in the pool, consistent lengths,
+    tables wide enough.  Raises ValueError naming what is violated."""
+    checks = [("history KV write", validate_store(plan.history_slots, num_blocks, block_size)),
+              ("step KV write", validate_store(plan.step_slots, num_blocks, block_size))]
+    if plan.prefill:
+        checks.append(("prefill", validate_prefill(
+            plan.cu_seqlens_q, plan.cu_seqlens_k, plan.prefill_block_tables, plan.max_seqlen_q,
+            plan.max_seqlen_k, num_blocks, block_size)))
+    if plan.decode:
+        checks.append(("decode", validate_decode(plan.context_lens, plan.decode_block_tables,
+                                                 plan.max_context_len, num_blocks, block_size)))
+    bad = [f"{what}: {'; '.join(contract_names(bits))}" for what, bits in checks if bits]
+    if bad:
+        raise ValueError("step metadata violates the data-plane contract: " + " | ".join(bad))
 
 # bit patterns used to poison pool memory no token writes
 STALE_BITS = {
@@ -56,6 +75,7 @@ class DeviceStep:
         self.plan = plan if plan is not None else plan_step(wl.seqs, wl.block_size, pool,
                                                             table_pad)
         p = self.plan
+        check_plan(p, wl.num_blocks, wl.block_size)
         dt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
         shape = (wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim)
         self.k_cache = torch.empty(shape, dtype=dt, device=self.device)
