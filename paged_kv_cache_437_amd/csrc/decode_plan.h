@@ -14,7 +14,15 @@
 
 namespace pkv {
 
-constexpr int kMaxAutoWorkers = 4096;  // bound on the automatic worker count
+// The automatic worker count: a constant of the stream shape, never read from the
+// device, so where streams are cut (and so the result bits) depends only on the
+// lengths and the shape.  One wave per SIMD of a 256-CU part while a stream holds up
+// to 4 q heads per kv head, two beyond: more concurrent streams read HBM less
+// efficiently, so the smallest count that keeps the vector work hidden is the
+// fastest (measured: at 4 q heads per kv head one wave per SIMD is 4-13% faster than
+// two; at 8, two are 8% faster; 1536 or 2560 workers ran 10-20% slower than the
+// multiples of 1024 around them).
+inline int auto_decode_workers(int GP) { return GP <= 4 ? 1024 : 2048; }
 
 // q heads per kv head in a stream for Hq / Hkv = G: G rounded up to a power of two,
 // at most 8

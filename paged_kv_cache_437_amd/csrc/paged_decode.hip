@@ -1,9 +1,6 @@
 // Paged decode attention, bf16 in / fp32 accumulate, for gfx950: the kernel and its
 // launchers.  The pass itself (what is computed, the work division, the loads) is in
 // decode_kernel.h.
-#include <algorithm>
-#include <atomic>
-
 #include "decode_kernel.h"
 
 namespace pkv {
@@ -29,34 +26,6 @@ paged_decode_bf16_kernel(
 namespace {
 
 template <int D, int GP, int MH, bool ONE_BLOCK>
-int auto_workers() {
-  static std::atomic<int> cached[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  int w = cached[dev].load(std::memory_order_relaxed);
-  if (w > 0) return w;
-  int cus = 0, per_cu = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu,
-          reinterpret_cast<const void*>(&paged_decode_bf16_kernel<D, GP, MH, ONE_BLOCK, false>),
-          256, 0) != hipSuccess ||
-      cus <= 0 || per_cu <= 0) {
-    cus = 256;
-    per_cu = 2;
-  }
-  // Waves per SIMD: one while each byte streamed costs little arithmetic (up to 4 q
-  // heads per kv head), two beyond (the VALU then needs a second wave to hide behind).
-  // Measured: more concurrent streams read HBM less efficiently, so the smallest count
-  // that keeps the arithmetic hidden is the fastest (at 4 q heads per kv head one wave
-  // per SIMD is 4-13% faster than two; at 8, two are 8% faster).  A whole number of
-  // workgroups per CU keeps the CUs evenly loaded.
-  w = std::min(kMaxAutoWorkers, cus * std::min(per_cu, GP <= 4 ? 1 : 2) * 4);
-  cached[dev].store(w, std::memory_order_relaxed);
-  return w;
-}
-
-template <int D, int GP, int MH, bool ONE_BLOCK>
 hipError_t launch_decode(const void* q, void* out, const void* k_cache, const void* v_cache,
                          int num_q_heads, int num_kv_heads, int bs_log2, int batch,
                          const int32_t* context_lens, const int32_t* block_tables,
@@ -66,7 +35,7 @@ hipError_t launch_decode(const void* q, void* out, const void* k_cache, const vo
   const int n_hg = (G + GP - 1) / GP;
   const int S = (num_kv_heads / MH) * n_hg;
   if (S > 65535) return hipErrorInvalidConfiguration;
-  const int W = num_workers > 0 ? num_workers : auto_workers<D, GP, MH, ONE_BLOCK>();
+  const int W = num_workers > 0 ? num_workers : auto_decode_workers(GP);
   const DecodeWorkspace ws = carve_decode_workspace(workspace, batch, W, MH * GP);
   const float scale_log2 = scale * kLog2e;
   timing_begin("paged_decode", stream);
@@ -126,26 +95,18 @@ hipError_t launch_decode_gp(int GP, const void* q, void* out, const void* k_cach
 }  // namespace
 
 int paged_decode_bf16_workers(int head_dim, int num_q_heads, int num_kv_heads, int bs_log2) {
-  const int GP = heads_per_stream(num_q_heads / num_kv_heads);
-  const int MH = kv_heads_per_stream(head_dim, num_kv_heads, num_q_heads / num_kv_heads);
-  const bool one = (1 << bs_log2) >= chunk_tokens(head_dim, MH);
-#define PKV_W(D_, GP_, MH_)                                                   \
-  if (head_dim == D_ && GP == GP_ && MH == MH_)                               \
-    return one ? auto_workers<D_, GP_, MH_, true>() : auto_workers<D_, GP_, MH_, false>();
-#define PKV_W_GP(D_, MH_) PKV_W(D_, 1, MH_) PKV_W(D_, 2, MH_) PKV_W(D_, 4, MH_) PKV_W(D_, 8, MH_)
-  PKV_W_GP(128, 1) PKV_W_GP(128, 2) PKV_W_GP(128, 4)
-  PKV_W_GP(64, 1) PKV_W_GP(64, 2) PKV_W_GP(64, 4) PKV_W_GP(64, 8)
-#undef PKV_W_GP
-#undef PKV_W
-  return kMaxAutoWorkers;
+  (void)head_dim;
+  (void)num_kv_heads;
+  (void)bs_log2;
+  return auto_decode_workers(heads_per_stream(num_q_heads / num_kv_heads));
 }
 
 size_t paged_decode_bf16_workspace(int head_dim, int num_q_heads, int num_kv_heads, int batch,
                                    int num_workers) {
   const int GP = heads_per_stream(num_q_heads / num_kv_heads);
   const int MH = kv_heads_per_stream(head_dim, num_kv_heads, num_q_heads / num_kv_heads);
-  return decode_workspace_bytes(batch, num_workers > 0 ? num_workers : kMaxAutoWorkers, MH * GP,
-                                head_dim);
+  return decode_workspace_bytes(batch, num_workers > 0 ? num_workers : auto_decode_workers(GP),
+                                MH * GP, head_dim);
 }
 
 hipError_t launch_paged_decode_bf16(int head_dim, const void* q, void* out, const void* k_cache,
