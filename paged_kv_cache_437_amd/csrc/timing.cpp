@@ -48,15 +48,22 @@ void timing_begin(const char* kernel, hipStream_t stream) {
   if (!g_on.load(std::memory_order_relaxed)) return;
   std::lock_guard<std::mutex> lk(g_mu);
   t_open = {kernel, take_event(), take_event()};
-  if (t_open.start) hipEventRecord(t_open.start, stream);
+  // a start event that could not be recorded drops this launch from the timing
+  if (t_open.start && hipEventRecord(t_open.start, stream) != hipSuccess) {
+    if (t_open.stop) g_spare.push_back(t_open.stop);
+    g_spare.push_back(t_open.start);
+    t_open = {nullptr, nullptr, nullptr};
+  }
 }
 
 void timing_end(hipStream_t stream) {
   if (!g_on.load(std::memory_order_relaxed) || t_open.kernel == nullptr) return;
   std::lock_guard<std::mutex> lk(g_mu);
-  if (t_open.start && t_open.stop) {
-    hipEventRecord(t_open.stop, stream);
+  if (t_open.start && t_open.stop && hipEventRecord(t_open.stop, stream) == hipSuccess) {
     g_pending.push_back(t_open);
+  } else {
+    if (t_open.start) g_spare.push_back(t_open.start);
+    if (t_open.stop) g_spare.push_back(t_open.stop);
   }
   t_open = {nullptr, nullptr, nullptr};
 }
