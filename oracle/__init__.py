@@ -16,8 +16,9 @@ Contents and what pins each part (tests/test_oracle.py):
   relabelling / prefix copies / stale poisoning, decode == last prefill row,
   split merge == unsplit, float32 vs float64 agreement, and planted mistakes
   that each of those must catch.
-* ``block_manager`` - the pages' BlockManager (free deque, reference counts,
-  prefix sharing) and the step planner.  Pinned by hand-worked allocation
+* ``block_manager`` - the pages' block allocation (a fixed pool of ids with
+  reference counts, a first-in first-out queue of free ids, prefix sharing) and
+  the step planner.  Pinned by hand-worked allocation
   fixtures, reference-count and exhaustion invariants, and slot round trips.
   ``PrefixCache`` models the prefix-cached manager keyed by whole token prefixes;
   pinned by the hand-worked scenarios of tests/test_block_manager.py and the
@@ -30,7 +31,7 @@ Contents and what pins each part (tests/test_oracle.py):
 
 Everything is float64 unless a caller asks for float32; nothing is tuned.
 """
-from .block_manager import Block, BlockManager, PrefixCache, cumulative_lengths, plan_step, slot_of
+from .block_manager import IdPool, PrefixCache, cumulative_lengths, plan_step, slot_of
 from .paged_attention import (as_float, bf16_bits_to_float, causal_attention, combine_partials,
                               decode_split_partials, gather_tokens, kv_head_of, paged_decode,
                               paged_prefill, store_kvcache)

@@ -1,23 +1,22 @@
 """Plain CPU model of the KV-cache control plane (test infrastructure only).
 
-Follows the BlockManager the pages describe (“Nano-vLLM 引擎架构解析”, section 3.2
+What the pages say the control plane does (“Nano-vLLM 引擎架构解析”, section 3.2
 "PagedAttention"; “深入 Nano-vLLM 推理引擎”, headings "Handling resource exhaustion",
-"From Sequences to Blocks", "Prefix Caching by hashing", "Control plane vs.
-data plane"):
+"From Sequences to Blocks", "Prefix Caching by hashing", "Control plane vs. data
+plane"), modelled as directly as possible:
 
-* a ``Block`` carries an id, a reference count and its token ids;
-* the manager keeps a deque of free blocks and a map of used ones and hands out
-  the free block at the head of the deque;
-* a sequence is cut into fixed-size blocks, never sharing a block with another
-  sequence except for a shared prefix, whose block ids are reused with their
-  reference counts raised;
-* freeing only marks a block free: its GPU contents are not cleared.
+* the KV pool is a fixed set of block ids; each id has a reference count, zero
+  meaning the block is free;
+* free ids wait in a first-in first-out queue and a request takes the oldest one;
+* a sequence's tokens fill its own blocks in order, except that a cached prefix is
+  reused by listing the same ids again, each reuse adding one reference;
+* releasing a reference that was the last one puts the id back at the end of the
+  queue; the block's GPU contents are left as they are.
 
-Reading where the pages disagree: the printed ``allocate`` invents a new block id
-when the free deque is empty, which would grow a fixed pool without bound and
-clash with live ids; here the pool is fixed and allocation fails (returns None),
-which is when the scheduler preempts a sequence.  A freed block goes to the tail
-of the free deque.
+Reading where the pages disagree: the printed allocation routine makes up a new id
+when nothing is free, which would grow a fixed pool and collide with live ids; here
+a request on an empty queue fails (``take`` returns None), which is the point where
+the scheduler preempts a sequence.
 
 ``plan_step`` turns a workload into the per-step metadata the data plane needs:
 block tables, the slot of every token written, cumulative sequence lengths for
@@ -29,45 +28,40 @@ from collections import deque
 
 import numpy as np
 
-__all__ = ["Block", "BlockManager", "PrefixCache", "slot_of", "cumulative_lengths", "plan_step"]
+__all__ = ["IdPool", "PrefixCache", "slot_of", "cumulative_lengths", "plan_step"]
 
 
-class Block:
-    def __init__(self, block_id: int):
-        self.block_id = block_id
-        self.ref_count = 0
-        self.token_ids = []
+class IdPool:
+    """Block ids 0 .. num_blocks-1 with reference counts and a queue of free ids
+    (initially ``free_order``, else id order)."""
 
-
-class BlockManager:
     def __init__(self, num_blocks: int, free_order=None):
-        order = range(num_blocks) if free_order is None else [int(b) for b in free_order]
-        self.blocks = [Block(i) for i in range(num_blocks)]
-        self.free_blocks = deque(order)
-        self.used_blocks = {}
+        self.refs = [0] * num_blocks
+        self.free_ids = list(range(num_blocks)) if free_order is None else [int(b) for b in free_order]
 
-    def allocate(self):
-        """Head of the free deque, reference count 1; None when the pool is empty."""
-        if not self.free_blocks:
+    def take(self):
+        """The oldest free id with one reference, or None when every id is in use."""
+        if len(self.free_ids) == 0:
             return None
-        block_id = self.free_blocks.popleft()
-        block = self.blocks[block_id]
-        block.ref_count = 1
-        block.token_ids = []
-        self.used_blocks[block_id] = block
-        return block_id
+        b = self.free_ids.pop(0)
+        self.refs[b] = 1
+        return b
 
-    def share(self, block_id: int) -> None:
-        """Reuse a cached block: one more reference, no copy."""
-        self.used_blocks[block_id].ref_count += 1
+    def retain(self, b: int) -> None:
+        """One more reference to an id in use (a shared cached block; nothing copied)."""
+        assert self.refs[b] > 0, "retain of a free block"
+        self.refs[b] += 1
 
-    def free(self, block_id: int) -> None:
-        """Drop one reference; at zero the block returns to the free deque (not cleared)."""
-        block = self.used_blocks[block_id]
-        block.ref_count -= 1
-        if block.ref_count == 0:
-            del self.used_blocks[block_id]
-            self.free_blocks.append(block_id)
+    def release(self, b: int) -> None:
+        """One reference fewer; the last one sends the id to the back of the queue."""
+        assert self.refs[b] > 0, "release of a free block"
+        self.refs[b] -= 1
+        if self.refs[b] == 0:
+            self.free_ids.append(b)
+
+    def in_use(self) -> dict:
+        """{id: reference count} of every id in use."""
+        return {b: r for b, r in enumerate(self.refs) if r > 0}
 
 
 def slot_of(table_row, position: int, block_size: int) -> int:
@@ -87,9 +81,9 @@ def cumulative_lengths(lengths) -> list:
 def plan_step(wl, table_pad: int = -1) -> dict:
     """Allocate every sequence's blocks in order and build the step's metadata.
 
-    Sequences take blocks from the free deque in index order; a sequence in a
+    Sequences take blocks from the free queue in index order; a sequence in a
     prefix group other than the group's first reuses the first one's prefix
-    blocks (``share``) and allocates the rest.  Returns plain Python lists:
+    blocks (``retain``) and takes the rest.  Returns plain Python lists:
 
     tables            per sequence, its block ids
     history_slots     (seq, position, slot) of tokens written before the step
@@ -101,7 +95,7 @@ def plan_step(wl, table_pad: int = -1) -> dict:
                       widest table of the step
     """
     bs = wl.block_size
-    mgr = BlockManager(wl.num_blocks, wl.free_order)
+    pool = IdPool(wl.num_blocks, wl.free_order)
     tables = []
     group_owner = {}
     for i, s in enumerate(wl.seqs):
@@ -110,12 +104,12 @@ def plan_step(wl, table_pad: int = -1) -> dict:
         if s.prefix_group >= 0 and s.prefix_group in group_owner:
             owner_table = tables[group_owner[s.prefix_group]]
             for j in range(s.prefix_len // bs):
-                mgr.share(owner_table[j])
+                pool.retain(owner_table[j])
                 table.append(owner_table[j])
         elif s.prefix_group >= 0:
             group_owner[s.prefix_group] = i
         while len(table) < n_blocks:
-            b = mgr.allocate()
+            b = pool.take()
             if b is None:
                 raise RuntimeError("pool exhausted")
             table.append(b)
@@ -138,7 +132,7 @@ def plan_step(wl, table_pad: int = -1) -> dict:
 
     return {
         "tables": tables,
-        "ref_counts": {b: blk.ref_count for b, blk in mgr.used_blocks.items()},
+        "ref_counts": pool.in_use(),
         "history_slots": history,
         "step_slots": step,
         "prefill": prefill,

@@ -85,26 +85,26 @@ def pin_golden_block_manager():
     assert plan["cu_seqlens_k"] == g["cu_seqlens_k"]
     assert plan["context_lens"] == g["context_lens"]
     # the same allocation step by step, then free sequence 3
-    mgr = bm.BlockManager(g["num_blocks"], g["free_order"])
+    pool = bm.IdPool(g["num_blocks"], g["free_order"])
     tables = []
     for i, s in enumerate(seqs):
         t = []
         if i == 3:
-            mgr.share(tables[2][0])
+            pool.retain(tables[2][0])
             t.append(tables[2][0])
         while len(t) < -(-s.context_len // g["block_size"]):
-            t.append(mgr.allocate())
+            t.append(pool.take())
         tables.append(t)
-    assert list(mgr.free_blocks) == g["free_after"], "free deque after allocation"
+    assert list(pool.free_ids) == g["free_after"], "free queue after allocation"
     for b in tables[3]:
-        mgr.free(b)
+        pool.release(b)
     after = g["free_sequence_3"]
-    assert list(mgr.free_blocks) == after["free_after"], "free deque after freeing seq 3"
-    assert {str(b): blk.ref_count for b, blk in mgr.used_blocks.items()} == after["ref_counts"]
+    assert list(pool.free_ids) == after["free_after"], "free queue after freeing seq 3"
+    assert {str(b): r for b, r in pool.in_use().items()} == after["ref_counts"]
     # exhaustion: the pool is fixed, allocation fails instead of inventing ids
-    while mgr.allocate() is not None:
+    while pool.take() is not None:
         pass
-    assert mgr.allocate() is None and len(mgr.used_blocks) == g["num_blocks"]
+    assert pool.take() is None and len(pool.in_use()) == g["num_blocks"]
 
 
 # ----------------------------------------------------------------------------- brute force

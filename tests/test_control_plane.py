@@ -1,5 +1,5 @@
 """Control plane (row a1): the product's vectorised planner against the oracle's
-plain BlockManager, bit for bit, plus pool invariants.  No GPU."""
+plain allocation model, bit for bit, plus pool invariants.  No GPU."""
 import numpy as np
 import pytest
 

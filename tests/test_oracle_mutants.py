@@ -93,18 +93,17 @@ def _decode_drops_newest(q, k_cache, v_cache, block_tables, context_lens, scale,
     return out
 
 
-class _LifoManager(bm.BlockManager):
-    def allocate(self):
-        if not self.free_blocks:
+class _LifoPool(bm.IdPool):
+    def take(self):
+        if not self.free_ids:
             return None
-        b = self.free_blocks.pop()
-        self.blocks[b].ref_count = 1
-        self.used_blocks[b] = self.blocks[b]
+        b = self.free_ids.pop()
+        self.refs[b] = 1
         return b
 
 
-class _NoShareManager(bm.BlockManager):
-    def share(self, block_id):
+class _NoSharePool(bm.IdPool):
+    def retain(self, b):
         pass
 
 
@@ -124,8 +123,8 @@ MUTANTS = {
     "combine_l_unweighted": [(pa, "combine_partials", _combine_unweighted_l)],
     "decode_drops_newest_key": [(pa, "paged_decode", _decode_drops_newest),
                                 (st, "paged_decode", _decode_drops_newest)],
-    "free_list_lifo": [(bm, "BlockManager", _LifoManager)],
-    "prefix_share_not_counted": [(bm, "BlockManager", _NoShareManager)],
+    "free_list_lifo": [(bm, "IdPool", _LifoPool)],
+    "prefix_share_not_counted": [(bm, "IdPool", _NoSharePool)],
 }
 
 
