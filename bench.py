@@ -1,28 +1,29 @@
 #!/usr/bin/env python3
 """Benchmark of the paged KV-cache hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--seed S]
-                    [--no-cpu-baseline] [--no-prefill]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--reps R] [--seed S]
+                    [--no-cpu-baseline] [--no-prefill] [--no-extras]
 
-A step is one pass of the hot path over one batch of synthetic input: the KV
-write of the batch's new tokens (one per sequence), then paged decode of the
-batch: a 7B-shaped layer (32 q / 32 kv heads, head_dim 128, block_size 256),
-32 sequences with context lengths uniform on [512, 4096], block ids a random
-permutation of a pool 1.25x the used blocks, bf16 with fp32 accumulation.  All
-inputs are resident in device memory before the timed region; the K timed steps
-are bracketed by a device synchronisation on both sides.
+A step is one pass of the hot path over one batch of synthetic input: the KV write of
+the batch's new tokens (one per sequence), then paged decode of the batch: a 7B-shaped
+layer (32 q / 32 kv heads, head_dim 128, block_size 256), 32 sequences with context
+lengths uniform on [512, 4096], block ids a random permutation of a pool 1.25x the used
+blocks, bf16 with fp32 accumulation.  All inputs are resident in device memory before
+the timed region; the K timed steps run back to back between two device
+synchronisations, and ``value`` is the step's algorithmic HBM bytes over that time.
 
-Printed: ONE JSON line.  ``value`` is the step's algorithmic HBM bytes (K and V
-of every context token, q, out, the new tokens' K/V read and written, and the
-metadata used) divided by the step time, timed without per-kernel events.
-``roofline`` is for the dominant kernel (decode): its duration is measured with
-HIP events recorded on its own stream around each launch, in a second timed pass
-over the same K steps.  ``prefill`` reports the varlen causal prefill (16 q /
-8 kv heads, 16 prompts of length uniform on [128, 2048]) in TFLOP/s over the
-unmasked causal pairs.  ``decode_large`` reports the large decode batch (256
-sequences, lognormal contexts, 32 q / 8 kv heads, pool at 60% of free memory) in
-GB/s.  ``cpu_baseline`` times the CPU oracle on a bounded sample of the same decode
-workload, on this host's cores.
+Per-kernel figures follow one protocol: W' = 5 untimed launches, then R (default 50)
+launches each timed on its own with HIP events recorded on the stream the kernel runs on
+(the library brackets its launches when timing is on), reported as the median with the
+10th and 90th percentiles.  Before every decode launch of that protocol a 512 MiB
+scratch buffer is written outside the timed region, so the 256 MB last-level cache
+cannot serve K/V.  ``roofline`` is the decode kernel of the headline step; ``prefill``
+the varlen causal prefill (16 q / 8 kv heads, 16 prompts of length uniform on
+[128, 2048]) in TFLOP/s over the unmasked causal pairs; ``prefill_shapes`` the
+prefix-cached prefill and long prompts; ``decode_large`` the large decode batch (256
+sequences, lognormal contexts, 32 q / 8 kv heads, pool at 60% of free memory) in GB/s.
+``cpu_baseline`` times the CPU oracle on a bounded sample of each configured workload,
+after the GPU legs, on this host's cores.
 """
 from __future__ import annotations
 
@@ -36,11 +37,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (256 CUs x 2.4 GHz x 4096 flop/clk/CU)
+FLUSH_BYTES = 512 << 20         # scratch written before each timed decode launch
 # rocprofv3 FETCH_SIZE / WRITE_SIZE summary of the decode kernel, with the hash of the
 # sources it was taken on (traffic is reported only while they are unchanged)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "paged_decode__decode_mha_bf16__traffic.txt")
 DECODE_SOURCES = ("paged_decode.hip", "decode_kernel.h", "decode_plan.h", "device.h")
-BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (256 CUs x 2.4 GHz x 4096 flop/clk/CU)
 
 
 def parse():
@@ -48,21 +50,26 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--reps", type=int, default=50,
+                    help="individually timed launches per kernel figure")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-only", action="store_true",
-                    help="time only the prefill leg (for profiling it alone)")
+                    help="time only the prefill legs (for profiling them alone)")
+    ap.add_argument("--decode-large-only", action="store_true",
+                    help="time only the large decode batch (for profiling it alone)")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the graph-replay and rotary comparisons (for profiling the "
-                         "decode step alone)")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="rough CPU budget of the oracle baseline sample")
+                    help="skip the graph-replay, rotary, mixed-step and large-batch legs")
+    ap.add_argument("--cpu-seconds", type=float, default=6.0,
+                    help="rough CPU budget of the oracle baseline, per configured workload")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB device to device 5 times (a plain copy kernel of "
                          "known size, to scale HBM byte counters against)")
     return ap.parse_args()
 
+
+# ---- algorithmic work (pinned by tests/test_bench_counts.py) ----
 
 def decode_bytes(wl, plan) -> int:
     """K and V of every context token, q read, out written, context lengths and the
@@ -118,11 +125,12 @@ def measured_traffic():
         return None
 
 
-def timed_steps(torch, pkv, fn, steps, kernel_events: bool):
-    """Run fn `steps` times between two device synchronisations; with kernel_events the
-    library brackets each of its launches with HIP events on the launch's stream."""
-    pkv.timing_collect()
-    pkv.timing_enable(kernel_events)
+# ---- timing ----
+
+def timed_steps(torch, pkv, fn, steps):
+    """fn run `steps` times back to back between two device synchronisations; returns
+    the elapsed milliseconds (events on torch's current stream, where the library
+    launches) and the host wall time."""
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -131,63 +139,75 @@ def timed_steps(torch, pkv, fn, steps, kernel_events: bool):
         fn()
     end.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    pkv.timing_enable(False)
-    return start.elapsed_time(end), wall, pkv.timing_collect()
+    return start.elapsed_time(end), time.perf_counter() - t0
 
 
-def cpu_baseline(wl, budget_s: float) -> dict:
-    """The CPU oracle, as it stands, on a bounded sample of the decode step: the KV
-    write of the step's new tokens, then decode of sequences in order until the
-    budget is spent (at least one)."""
+def _quantiles(xs):
     import numpy as np
+    a = np.asarray(xs, dtype=np.float64)
+    return {"median": float(np.median(a)), "p10": float(np.percentile(a, 10)),
+            "p90": float(np.percentile(a, 90)), "mean": float(a.mean()), "n": int(a.size)}
 
-    import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:  # noqa: BLE001 - threadpoolctl missing: report the affinity set
-        threads = len(os.sched_getaffinity(0))
-    plan = oracle.plan_step(wl)
-    hist = {"history_slots": plan["history_slots"], "step_slots": []}
-    k_cache, v_cache = oracle.build_caches(wl, hist)
-    step_rows = plan["step_slots"]
-    k_new = np.stack([wl.k[i][p] for (i, p, _) in step_rows])
-    v_new = np.stack([wl.v[i][p] for (i, p, _) in step_rows])
-    t0 = time.perf_counter()
-    oracle.store_kvcache(k_cache, v_cache, k_new, v_new, [s for (_, _, s) in step_rows])
-    done_bytes = store_bytes(wl, len(step_rows))
-    n = 0
-    s = wl.elem_bytes
-    passes = 0
-    while True:  # whole passes over the batch until the budget is spent
-        for b, i in enumerate(plan["decode"]):
-            q = wl.q[i][:1]
-            oracle.paged_decode(q, k_cache, v_cache, plan["decode_block_tables"][b:b + 1],
-                                plan["context_lens"][b:b + 1], wl.scale)
-            L = plan["context_lens"][b]
-            done_bytes += (s * (2 * wl.num_kv_heads * wl.head_dim * L
-                                + 2 * wl.num_q_heads * wl.head_dim)
-                           + 4 * (1 + -(-L // wl.block_size)))
-            n += 1
-            if time.perf_counter() - t0 >= budget_s:
-                break
-        passes += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    secs = time.perf_counter() - t0
-    cpu_model = "unknown"
-    try:
-        with open("/proc/cpuinfo") as f:
-            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f
-                              if ln.startswith("model name")), cpu_model)
-    except OSError:
-        pass
-    return {"value": done_bytes / secs / 1e9, "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle", "cpu_model": cpu_model,
-            "sample": f"KV write of the {len(step_rows)} new tokens + float64 decode of "
-                      f"{n} sequences ({passes} pass(es) over the {len(plan['decode'])}-sequence "
-                      f"batch, {secs:.1f} s)"}
+
+def per_launch(torch, pkv, fn, reps, warmup=5, flush=None):
+    """The protocol of every per-kernel figure: `warmup` untimed calls, then `reps` calls
+    each timed on its own (the library's HIP events around each of its kernel launches,
+    on the launch's stream), with `flush()` before each call outside the timed region.
+    Returns {kernel name: quantiles of its per-launch milliseconds}."""
+    for _ in range(warmup):
+        if flush is not None:
+            flush()
+        fn()
+    torch.cuda.synchronize()
+    pkv.timing_collect()
+    samples = {}
+    for _ in range(reps):
+        if flush is not None:
+            flush()
+        torch.cuda.synchronize()
+        pkv.timing_enable(True)
+        fn()
+        pkv.timing_enable(False)
+        for name, t in pkv.timing_collect().items():
+            samples.setdefault(name, []).extend([t["total_ms"] / t["launches"]] * t["launches"])
+    return {k: _quantiles(v) for k, v in samples.items()}
+
+
+def _rate(work, q, unit_scale):
+    """Work per launch over the median duration, and over the p90 / p10 durations
+    (the low and high ends of the rate)."""
+    r = lambda ms: work / (ms * 1e-3) / unit_scale
+    return round(r(q["median"]), 2), round(r(q["p90"]), 2), round(r(q["p10"]), 2)
+
+
+def make_flush(torch):
+    scratch = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    state = {"i": 0}
+
+    def flush():
+        state["i"] = (state["i"] + 1) & 0x7F
+        scratch.fill_(state["i"])
+    return flush
+
+
+# ---- legs ----
+
+def decode_roofline(torch, pkv, step, d_bytes, args, flush):
+    """The decode kernel of the headline step under the per-launch protocol."""
+    q = per_launch(torch, pkv, step.run, args.reps, flush=flush)
+    name = max((k for k in q if k.startswith("paged_decode") and "combine" not in k),
+               key=lambda k: q[k]["median"])
+    med, lo, hi = _rate(d_bytes, q[name], 1e9)
+    return {"kernel": name, "bound": "hbm", "achieved": med, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(med / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+            "achieved_p10": lo, "achieved_p90": hi,
+            "frac_p10": round(lo / HBM_PEAK_GBS, 4), "frac_p90": round(hi / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes_per_launch": d_bytes,
+            "launch_ms": {k: round(v, 5) for k, v in q[name].items() if k != "n"},
+            "launches": q[name]["n"],
+            "protocol": f"5 warm-ups, {q[name]['n']} launches each timed alone, 512 MiB "
+                        "scratch written before each; median (p10/p90)",
+            "kernels_median_ms": {k: round(v["median"], 5) for k, v in q.items()}}
 
 
 def graph_step(torch, pkv, step, wl, args) -> dict:
@@ -202,8 +222,8 @@ def graph_step(torch, pkv, step, wl, args) -> dict:
               step.context_lens)
     for _ in range(args.warmup):
         graph.graph.replay()
-    g_ms, _, _ = timed_steps(torch, pkv, graph.graph.replay, args.steps, kernel_events=False)
-    e_ms, _, _ = timed_steps(torch, pkv, step.run, args.steps, kernel_events=False)
+    g_ms, _ = timed_steps(torch, pkv, graph.graph.replay, args.steps)
+    e_ms, _ = timed_steps(torch, pkv, step.run, args.steps)
     del graph
     return {"eager_ms_per_step": round(e_ms / args.steps, 5),
             "graph_ms_per_step": round(g_ms / args.steps, 5)}
@@ -226,61 +246,74 @@ def small_decode_graph(torch, pkv, workloads, DeviceStep, args) -> dict:
     return out
 
 
-def prefill_shapes(torch, pkv, workloads, DeviceStep, args) -> dict:
-    """Prefill TFLOP/s on the prefix-cached workload (64 sequences, 1024 shared prefix
-    tokens + 256 own, suffix queries only, 32/8 heads) and on long causal prompts
-    (4 x 8192 tokens, 32/8 heads), beside the varlen headline."""
-    from workloads import SeqSpec
-    out = {}
-    for name, wl in (("prefill_prefix_cached", workloads.prefill_prefix_cached(seed=args.seed)),
-                     ("causal_4x8192_32q8kv", workloads.custom(
-                         "long_bf16", "bf16", 32, 8, 128, 256,
-                         [SeqSpec("prefill", 8192, 8192)] * 4, seed=args.seed))):
-        st = DeviceStep(wl, device="cuda", stale=None)
-        st.run()
-        torch.cuda.synchronize()
-        _, _, pk = timed_steps(torch, pkv, st.prefill, 5, kernel_events=True)
-        pname = max((k for k in pk if "prefill" in k), key=lambda k: pk[k]["total_ms"])
-        tf = prefill_flops(wl, st.plan) / (pk[pname]["avg_ms"] * 1e-3) / 1e12
-        out[name] = {"avg_launch_ms": round(pk[pname]["avg_ms"], 5), "TFLOP/s": round(tf, 2),
-                     "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4)}
-        del st
-        torch.cuda.empty_cache()
+def prefill_leg(torch, pkv, wp, DeviceStep, args, rotary: bool = False) -> dict:
+    """Prefill TFLOP/s of one workload under the per-launch protocol, and its KV write of
+    all the prompts' tokens (HBM-bound at these sizes) in GB/s."""
+    table = pkv.rotary_table(max(4096, max(s.context_len for s in wp.seqs)), wp.head_dim) \
+        if rotary else None
+    ps = DeviceStep(wp, device="cuda", stale="nan", rotary=table)
+    ps.run()
+    torch.cuda.synchronize()
+    q = per_launch(torch, pkv, ps.prefill, args.reps)
+    pname = max((k for k in q if "prefill" in k), key=lambda k: q[k]["median"])
+    flops = prefill_flops(wp, ps.plan)
+    med, lo, hi = _rate(flops, q[pname], 1e12)
+    out = {"kernel": pname, "bound": "mfma", "achieved": med, "peak": BF16_MFMA_PEAK_TFLOPS,
+           "unit": "TFLOP/s", "frac": round(med / BF16_MFMA_PEAK_TFLOPS, 4),
+           "achieved_p10": lo, "achieved_p90": hi,
+           "algorithmic_flops_per_launch": flops,
+           "launch_ms": {k: round(v, 5) for k, v in q[pname].items() if k != "n"},
+           "launches": q[pname]["n"]}
+    sq = per_launch(torch, pkv, ps.store, args.reps)
+    sname = next(k for k in sq if k.startswith("store_kvcache"))  # with or without rotary
+    n_tok = len(ps.plan.step_slots)
+    s_med, s_lo, s_hi = _rate(store_bytes(wp, n_tok), sq[sname], 1e9)
+    out["store_kvcache"] = {"tokens": n_tok, "bytes_per_launch": store_bytes(wp, n_tok),
+                            "kernel": sname, "median_launch_ms": round(sq[sname]["median"], 5),
+                            "achieved": s_med, "achieved_p10": s_lo, "achieved_p90": s_hi,
+                            "unit": "GB/s", "frac": round(s_med / HBM_PEAK_GBS, 4)}
+    del ps
+    torch.cuda.empty_cache()
     return out
 
 
-def decode_large_leg(torch, pkv, workloads, DeviceStep, args) -> dict:
+def decode_large_leg(torch, pkv, workloads, DeviceStep, args, flush):
     """The large decode batch: 256 sequences, ln(context) ~ N(ln 2048, 1) clipped to
     [64, 16384], 32 q / 8 kv heads, head_dim 128, block_size 256, the pool sized to 60%
-    of free device memory with the used blocks scattered over it.  Reports the decode
-    kernel's algorithmic HBM rate (events around each launch) and the whole step's."""
+    of free device memory with the used blocks scattered over it.  The decode kernel's
+    algorithmic HBM rate under the per-launch protocol (each launch alone, after the
+    scratch write: never right after a back-to-back pass), and the whole step's rate
+    back to back."""
     free, _ = torch.cuda.mem_get_info()
     bb = workloads.block_bytes(256, 8, 128, 2)
     wl = workloads.decode_large(seed=args.seed, pool_blocks=int(0.6 * free // bb))
     st = DeviceStep(wl, device="cuda", stale=None)
+    q = per_launch(torch, pkv, st.run, args.reps, flush=flush)
+    steps = max(5, args.steps // 5)
     for _ in range(3):
         st.run()
-    torch.cuda.synchronize()
-    steps = max(5, args.steps // 5)
-    ms, _, _ = timed_steps(torch, pkv, st.run, steps, kernel_events=False)
-    _, _, kernels = timed_steps(torch, pkv, st.run, steps, kernel_events=True)
+    ms, _ = timed_steps(torch, pkv, st.run, steps)
     d_bytes = decode_bytes(wl, st.plan)
     s_bytes = store_bytes(wl, len(st.plan.step_slots))
-    dec = kernels["paged_decode"]
-    gbs = d_bytes / (dec["avg_ms"] * 1e-3) / 1e9
+    name = max((k for k in q if k.startswith("paged_decode") and "combine" not in k),
+               key=lambda k: q[k]["median"])
+    med, lo, hi = _rate(d_bytes, q[name], 1e9)
     out = {"workload": "decode_large_bf16: 256 seqs, ln ctx ~ N(ln 2048, 1) clipped [64, 16384], "
                        "32 q / 8 kv heads, head_dim 128, block_size 256, pool 60% of free HBM",
            "sum_context": int(sum(s.context_len for s in wl.seqs)),
-           "pool_blocks": wl.num_blocks,
-           "decode_avg_launch_ms": round(dec["avg_ms"], 5),
-           "merge_avg_launch_ms": round(kernels.get("paged_decode_combine", {"avg_ms": 0.0})["avg_ms"], 5),
+           "pool_blocks": wl.num_blocks, "kernel": name,
            "algorithmic_bytes_per_launch": d_bytes,
-           "achieved": round(gbs, 2), "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-           "step_ms": round(ms / steps, 5),
-           "step_GB/s": round((d_bytes + s_bytes) / (ms / steps * 1e-3) / 1e9, 2)}
+           "achieved": med, "achieved_p10": lo, "achieved_p90": hi, "unit": "GB/s",
+           "frac": round(med / HBM_PEAK_GBS, 4), "frac_p10": round(lo / HBM_PEAK_GBS, 4),
+           "frac_p90": round(hi / HBM_PEAK_GBS, 4),
+           "launch_ms": {k: round(v, 5) for k, v in q[name].items() if k != "n"},
+           "launches": q[name]["n"],
+           "merge_median_ms": round(q.get("paged_decode_combine", {"median": 0.0})["median"], 5),
+           "step_ms_back_to_back": round(ms / steps, 5),
+           "step_GB/s_back_to_back": round((d_bytes + s_bytes) / (ms / steps * 1e-3) / 1e9, 2)}
     del st
     torch.cuda.empty_cache()
-    return out
+    return out, wl
 
 
 def mixed_leg(torch, pkv, workloads, DeviceStep, args) -> dict:
@@ -298,8 +331,8 @@ def mixed_leg(torch, pkv, workloads, DeviceStep, args) -> dict:
     for _ in range(args.warmup):
         two()
         st.mixed()
-    t_ms, _, _ = timed_steps(torch, pkv, two, args.steps, kernel_events=False)
-    m_ms, _, _ = timed_steps(torch, pkv, st.mixed, args.steps, kernel_events=False)
+    t_ms, _ = timed_steps(torch, pkv, two, args.steps)
+    m_ms, _ = timed_steps(torch, pkv, st.mixed, args.steps)
     del st
     return {"workload": "32 decode seqs ctx U[512, 4096] + 8 prompts U[128, 2048], 32 q / 32 kv "
                         "heads, head_dim 128, block_size 256 (attention only, KV written before)",
@@ -307,38 +340,88 @@ def mixed_leg(torch, pkv, workloads, DeviceStep, args) -> dict:
             "one_launch_ms": round(m_ms / args.steps, 5)}
 
 
-def prefill_leg(torch, pkv, workloads, DeviceStep, args, rotary: bool = False) -> dict:
-    """Varlen causal prefill (16 prompts, lengths uniform on [128, 2048]) in TFLOP/s;
-    with ``rotary`` the queries are rotated in the kernel's prologue (and K on write)."""
-    wp = workloads.prefill_varlen(seed=args.seed)
-    table = pkv.rotary_table(4096, wp.head_dim) if rotary else None
-    ps = DeviceStep(wp, device="cuda", stale="nan", rotary=table)
-    for _ in range(3):
-        ps.run()
-    torch.cuda.synchronize()
-    _, _, pk = timed_steps(torch, pkv, ps.prefill, max(5, args.steps // 5), kernel_events=True)
-    pname = max((k for k in pk if "prefill" in k), key=lambda k: pk[k]["total_ms"])
-    flops = prefill_flops(wp, ps.plan)
-    tflops = flops / (pk[pname]["avg_ms"] * 1e-3) / 1e12
-    # the KV write of all the prompts' tokens (HBM-bound at this size)
-    _, _, sk = timed_steps(torch, pkv, ps.store, max(5, args.steps // 5), kernel_events=True)
-    n_tok = len(ps.plan.step_slots)
-    sname = next(k for k in sk if k.startswith("store_kvcache"))  # with or without rotary
-    s_gbs = store_bytes(wp, n_tok) / (sk[sname]["avg_ms"] * 1e-3) / 1e9
-    del ps
-    torch.cuda.empty_cache()
-    return {
-        "store_kvcache": {"tokens": n_tok, "bytes_per_launch": store_bytes(wp, n_tok),
-                          "kernel": sname, "avg_launch_ms": round(sk[sname]["avg_ms"], 5),
-                          "achieved": round(s_gbs, 2), "unit": "GB/s",
-                          "frac": round(s_gbs / HBM_PEAK_GBS, 4)},
-        "workload": "prefill_varlen_bf16: 16 prompts, lengths uniform [128, 2048], "
-                    "16 q / 8 kv heads, head_dim 128, block_size 256",
-        "kernel": pname, "bound": "mfma", "achieved": round(tflops, 2),
-        "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-        "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
-        "algorithmic_flops_per_launch": flops, "avg_launch_ms": round(pk[pname]["avg_ms"], 5),
-    }
+# ---- the CPU oracle baseline ----
+
+def _cpu_info():
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # noqa: BLE001 - threadpoolctl missing: report the affinity set
+        threads = len(os.sched_getaffinity(0))
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f
+                              if ln.startswith("model name")), cpu_model)
+    except OSError:
+        pass
+    return int(threads), cpu_model
+
+
+def cpu_baseline_of(wl, budget_s: float, what: str) -> dict:
+    """The CPU oracle, as it stands, on a bounded sample of one workload: the step's KV
+    write, then its sequences in order (decode, or prefill) until the budget is spent
+    (at least one).  Reported in the unit of the workload's GPU figure: GB/s of
+    algorithmic bytes for decode, TFLOP/s of unmasked causal pairs for prefill."""
+    import numpy as np
+
+    import oracle
+    plan = oracle.plan_step(wl)
+    k_cache, v_cache = oracle.build_caches(wl, {"history_slots": plan["history_slots"],
+                                                "step_slots": []})
+    rows = plan["step_slots"]
+    k_new = np.stack([wl.k[i][p] for (i, p, _) in rows])
+    v_new = np.stack([wl.v[i][p] for (i, p, _) in rows])
+    s = wl.elem_bytes
+    t0 = time.perf_counter()
+    oracle.store_kvcache(k_cache, v_cache, k_new, v_new, [x for (_, _, x) in rows])
+    work, n = 0, 0
+    seqs = plan["decode"] if what == "decode" else plan["prefill"]
+    for b, i in enumerate(seqs):
+        if what == "decode":
+            L = plan["context_lens"][b]
+            oracle.paged_decode(wl.q[i][:1], k_cache, v_cache,
+                                block_tables=plan["decode_block_tables"][b:b + 1],
+                                context_lens=[L], scale=wl.scale)
+            work += (s * (2 * wl.num_kv_heads * wl.head_dim * L + 2 * wl.num_q_heads * wl.head_dim)
+                     + 4 * (1 + -(-L // wl.block_size)))
+        else:
+            Lq, Lk = wl.seqs[i].new_tokens, wl.seqs[i].context_len
+            oracle.paged_prefill(wl.q[i], k_cache, v_cache, cu_seqlens_q=[0, Lq],
+                                 cu_seqlens_k=[0, Lk],
+                                 block_tables=plan["prefill_block_tables"][b:b + 1],
+                                 scale=wl.scale)
+            work += 4 * wl.head_dim * wl.num_q_heads * (Lq * (Lk - Lq) + Lq * (Lq + 1) // 2)
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    secs = time.perf_counter() - t0
+    threads, cpu_model = _cpu_info()
+    unit, scale = ("GB/s", 1e9) if what == "decode" else ("TFLOP/s", 1e12)
+    return {"value": round(work / secs / scale, 5), "unit": unit, "cores": threads,
+            "kind": "oracle", "cpu_model": cpu_model,
+            "sample": f"{wl.name}: KV write of the step's {len(rows)} new tokens + float64 "
+                      f"{what} of {n} of its {len(seqs)} sequences in order ({secs:.1f} s)"}
+
+
+def cpu_baselines(workloads, args, wl_large) -> dict:
+    """One oracle timing per configured workload (the large decode batch on a pool of
+    1.25x its used blocks: the oracle's host arrays cannot hold the 60% pool, and its
+    per-sequence gather does not depend on the pool's size)."""
+    out = {"decode_mha": cpu_baseline_of(workloads.decode_mha(seed=args.seed), args.cpu_seconds,
+                                         "decode")}
+    for name in ("prefill_varlen", "prefill_prefix_cached"):
+        out[name] = cpu_baseline_of(workloads.by_name(name, seed=args.seed), args.cpu_seconds,
+                                    "prefill")
+    if wl_large is not None:
+        import copy
+
+        import numpy as np
+        small = copy.copy(wl_large)
+        small.num_blocks = -(-sum(-(-s.context_len // 256) for s in wl_large.seqs) * 5 // 4)
+        small.free_order = np.random.default_rng(args.seed).permutation(small.num_blocks)
+        out["decode_large"] = cpu_baseline_of(small, args.cpu_seconds, "decode")
+    return out
 
 
 def main():
@@ -376,9 +459,17 @@ def main():
               flush=True)
         return
 
+    flush = make_flush(torch)
     if args.prefill_only:
-        print(json.dumps({"prefill": prefill_leg(torch, pkv, workloads, DeviceStep, args)}),
-              flush=True)
+        out = {"prefill": prefill_leg(torch, pkv, workloads.prefill_varlen(seed=args.seed),
+                                      DeviceStep, args),
+               "prefill_prefix_cached": prefill_leg(
+                   torch, pkv, workloads.prefill_prefix_cached(seed=args.seed), DeviceStep, args)}
+        print(json.dumps(out), flush=True)
+        return
+    if args.decode_large_only:
+        print(json.dumps({"decode_large": decode_large_leg(torch, pkv, workloads, DeviceStep,
+                                                           args, flush)[0]}), flush=True)
         return
 
     # ---- decode step (the headline workload)
@@ -389,20 +480,15 @@ def main():
     for _ in range(args.warmup):
         step.run()
     torch.cuda.synchronize()
-    # The step time comes from a pass without per-kernel events (each event pair adds
-    # about 10 us of command-processor time before its launch); the kernel durations
-    # of the roofline come from a second timed pass over the same steps with them.
-    ms_total, wall, _ = timed_steps(torch, pkv, step.run, args.steps, kernel_events=False)
+    ms_total, wall = timed_steps(torch, pkv, step.run, args.steps)
     ms_per_step = ms_total / args.steps
-    _, _, kernels = timed_steps(torch, pkv, step.run, args.steps, kernel_events=True)
     d_bytes = decode_bytes(wl, plan)
     s_bytes = store_bytes(wl, n_new)
     value = (d_bytes + s_bytes) / (ms_per_step * 1e-3) / 1e9
-    graph_big = None if args.no_extras else graph_step(torch, pkv, step, wl, args)
-    decode_kernels = {k: v for k, v in kernels.items() if "decode" in k}
-    dom_name = max(decode_kernels, key=lambda k: decode_kernels[k]["total_ms"])
-    dom = decode_kernels[dom_name]
-    achieved = d_bytes / (dom["avg_ms"] * 1e-3) / 1e9
+    print(f"[bench] decode step: {ms_per_step:.4f} ms, {value:.1f} GB/s", file=sys.stderr,
+          flush=True)
+    roof = decode_roofline(torch, pkv, step, d_bytes, args, flush)
+    print(f"[bench] decode kernel: {roof['achieved']} GB/s median", file=sys.stderr, flush=True)
 
     result = {
         "metric": "paged decode HBM GB/s + prefill TFLOP/s, % of MI355X roofline",
@@ -426,59 +512,67 @@ def main():
             "pool_blocks": wl.num_blocks,
             "parallelism": "none (1 GPU)",
         },
-        "roofline": {
-            "kernel": dom_name,
-            "bound": "hbm",
-            "achieved": round(achieved, 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(),
-            "algorithmic_bytes_per_launch": d_bytes,
-            "avg_launch_ms": round(dom["avg_ms"], 5),
-        },
-        "kernels": {k: {"launches": v["launches"], "avg_ms": round(v["avg_ms"], 5)}
-                    for k, v in kernels.items()},
+        "roofline": roof,
     }
     if not args.no_extras:
         result["graph_step"] = {
             "what": "decode step (KV write + decode) eager vs replayed from a HIP graph",
-            "this_workload": graph_big,
+            "this_workload": graph_step(torch, pkv, step, wl, args),
             "launch_bound": small_decode_graph(torch, pkv, workloads, DeviceStep, args),
         }
-
-    # ---- the large decode batch, while device memory is still unfragmented (its pool
-    # takes 60% of it)
-    if not args.no_extras:
-        result["decode_large"] = decode_large_leg(torch, pkv, workloads, DeviceStep, args)
-
-    # ---- the same decode step with rotary position embedding fused in (K rotated in
-    # the KV write, the queries in the decode kernel)
-    if not args.no_extras:
+        # the same decode step with rotary position embedding fused in (K rotated in
+        # the KV write, the queries in the decode kernel)
         table = pkv.rotary_table(4096, wl.head_dim)
         rstep = DeviceStep(wl, device="cuda", stale="nan", rotary=table)
         for _ in range(args.warmup):
             rstep.run()
-        r_ms, _, _ = timed_steps(torch, pkv, rstep.run, args.steps, kernel_events=False)
+        r_ms, _ = timed_steps(torch, pkv, rstep.run, args.steps)
+        e_ms, _ = timed_steps(torch, pkv, step.run, args.steps)
         result["rotary"] = {"decode_ms_per_step": round(r_ms / args.steps, 5),
-                            "decode_value": round((d_bytes + s_bytes)
-                                                  / (r_ms / args.steps * 1e-3) / 1e9, 2),
-                            "unit": "GB/s"}
+                            "plain_decode_ms_per_step": round(e_ms / args.steps, 5)}
         del rstep
+    del step
+    torch.cuda.empty_cache()
 
-    # ---- varlen causal prefill, reported beside the decode line
+    # ---- the large decode batch (its pool takes 60% of free memory)
+    wl_large = None
+    if not args.no_extras:
+        result["decode_large"], wl_large = decode_large_leg(torch, pkv, workloads, DeviceStep,
+                                                            args, flush)
+        print(f"[bench] decode_large: {result['decode_large']['achieved']} GB/s median",
+              file=sys.stderr, flush=True)
+
+    # ---- prefill, reported beside the decode line
     if not args.no_prefill:
-        del step
-        torch.cuda.empty_cache()
-        result["prefill"] = prefill_leg(torch, pkv, workloads, DeviceStep, args)
+        result["prefill"] = prefill_leg(torch, pkv, workloads.prefill_varlen(seed=args.seed),
+                                        DeviceStep, args)
+        result["prefill"]["workload"] = ("prefill_varlen_bf16: 16 prompts, lengths uniform "
+                                         "[128, 2048], 16 q / 8 kv heads, head_dim 128, "
+                                         "block_size 256")
+        print(f"[bench] prefill: {result['prefill']['achieved']} TFLOP/s median",
+              file=sys.stderr, flush=True)
         if not args.no_extras:
-            result["rotary"]["prefill_tflops"] = prefill_leg(torch, pkv, workloads, DeviceStep,
-                                                             args, rotary=True)["achieved"]
+            from workloads import SeqSpec
+            shapes = {}
+            for name, w in (("prefill_prefix_cached", workloads.prefill_prefix_cached(seed=args.seed)),
+                            ("causal_4x8192_32q8kv", workloads.custom(
+                                "long_bf16", "bf16", 32, 8, 128, 256,
+                                [SeqSpec("prefill", 8192, 8192)] * 4, seed=args.seed))):
+                leg = prefill_leg(torch, pkv, w, DeviceStep, args)
+                shapes[name] = {k: leg[k] for k in ("achieved", "achieved_p10", "achieved_p90",
+                                                    "frac", "launch_ms", "launches",
+                                                    "algorithmic_flops_per_launch")}
+            result["prefill_shapes"] = shapes
+            result["rotary"]["prefill_varlen"] = {
+                k: v for k, v in prefill_leg(torch, pkv, workloads.prefill_varlen(seed=args.seed),
+                                             DeviceStep, args, rotary=True).items()
+                if k in ("achieved", "achieved_p10", "achieved_p90", "frac")}
             result["mixed_step"] = mixed_leg(torch, pkv, workloads, DeviceStep, args)
-            result["prefill_shapes"] = prefill_shapes(torch, pkv, workloads, DeviceStep, args)
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        per = cpu_baselines(workloads, args, wl_large)
+        result["cpu_baseline"] = dict(per["decode_mha"])
+        result["cpu_baseline"]["configs"] = per
 
     print(json.dumps(result), flush=True)
 
