@@ -199,6 +199,23 @@ pkv_status pkv_paged_decode_rotary(const pkv_cache* cache, const void* q, void* 
                                    int32_t num_workers, const pkv_rotary* rotary,
                                    hipStream_t stream);
 
+/* pkv_paged_decode (or pkv_paged_decode_rotary when rotary is not NULL) without a
+ * workspace argument, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.  The split-K
+ * workspace is a fixed 16 MiB device array of the library's own, one per GPU, held
+ * until the process ends; this call allocates nothing.  Results are bit-identical to
+ * pkv_paged_decode with the same num_workers.  A shape whose workspace
+ * (pkv_paged_decode_workspace_size) exceeds 16 MiB returns PKV_ERR_WORKSPACE: the
+ * automatic worker count fits for up to 4 q heads per kv head; with 8 or more ask for
+ * fewer workers (e.g. 480 at head_dim 128).  Calls on one GPU share its array: calls in
+ * flight on one GPU at once race.  Other arguments and errors as in pkv_paged_decode. */
+pkv_status pkv_paged_decode_noalloc(const pkv_cache* cache, const void* q, void* out,
+                                    int32_t num_q_heads, int32_t batch,
+                                    const int32_t* context_lens, int32_t max_context_len,
+                                    const int32_t* block_tables, int32_t block_table_stride,
+                                    float scale, int32_t num_workers, const pkv_rotary* rotary,
+                                    hipStream_t stream);
+
 /* One step's attention for a batch holding sequences in both phases (“深入 Nano-vLLM 推理引擎”,
  * "Prefill and Decode" and the scheduler headings: the running batch mixes prompts
  * being prefilled with sequences being decoded).  The prefill arguments are those of

@@ -31,7 +31,7 @@ from ._lib import PkvError
 __all__ = ["store_kvcache", "paged_prefill", "paged_decode", "paged_decode_workspace_size",
            "mixed_attention", "rotary_table", "PkvError", "version", "library_path", "timing_enable",
            "timing_collect", "validate_store", "validate_prefill", "validate_decode",
-           "contract_names", "debug_enable", "debug_enabled"]
+           "contract_names", "debug_enable", "debug_enabled", "paged_decode_noalloc"]
 
 _DTYPES = {torch.float32: _lib.PKV_F32, torch.bfloat16: _lib.PKV_BF16}
 
@@ -208,6 +208,32 @@ def paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     else:
         _lib.check(lib.pkv_paged_decode_rotary(ctypes.byref(desc), *args, ctypes.byref(rot),
                                                _stream(k_cache.device)))
+    return out
+
+
+def paged_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                         block_tables: torch.Tensor, context_lens: torch.Tensor,
+                         max_context_len: int, scale: float, out: torch.Tensor,
+                         num_workers: int = 0, rotary: torch.Tensor | None = None) -> torch.Tensor:
+    """paged_decode through the entry point that allocates nothing: its split-K
+    workspace is the library's fixed per-device array, and the caller passes ``out``."""
+    lib = _lib.load()
+    desc = _cache_desc(k_cache, v_cache)
+    if q.dim() != 3 or q.shape[2] != k_cache.shape[3]:
+        raise ValueError("q must be [B, Hq, D]")
+    batch = q.shape[0]
+    if context_lens.numel() != batch or block_tables.dim() != 2 or block_tables.shape[0] != batch:
+        raise ValueError("context_lens / block_tables disagree with q on batch")
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    rot = _rotary(rotary, k_cache)
+    _lib.check(lib.pkv_paged_decode_noalloc(
+        ctypes.byref(desc), _dev(q, "q", k_cache.dtype, k_cache),
+        _dev(out, "out", k_cache.dtype, k_cache), q.shape[1], batch,
+        _dev(context_lens, "context_lens", torch.int32, k_cache), int(max_context_len),
+        _dev(block_tables, "block_tables", torch.int32, k_cache), block_tables.shape[1],
+        float(scale), int(num_workers), None if rot is None else ctypes.byref(rot),
+        _stream(k_cache.device)))
     return out
 
 

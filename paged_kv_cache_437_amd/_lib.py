@@ -26,7 +26,7 @@ EXPORTED = (
     "pkv_bm_num_cached_tokens", "pkv_bm_num_tokens", "pkv_bm_can_append",
     "pkv_bm_append_token", "pkv_bm_deallocate", "pkv_bm_block_table",
     "pkv_validate_store", "pkv_validate_prefill", "pkv_validate_decode", "pkv_debug_enable",
-    "pkv_debug_enabled",
+    "pkv_debug_enabled", "pkv_paged_decode_noalloc",
 )
 
 # contract bits of pkv_validate_* (include/pkv.h)
@@ -107,6 +107,9 @@ def load() -> ctypes.CDLL:
     lib.pkv_mixed_attention.argtypes = [cache_p, I, ctypes.c_float, P, P, I, P, P, I, I, P, I,
                                         P, P, I, P, I, P, I, P, ctypes.c_size_t, I, rot_p, P]
     lib.pkv_mixed_attention.restype = I
+    lib.pkv_paged_decode_noalloc.argtypes = [cache_p, P, P, I, I, P, I, P, I, ctypes.c_float, I,
+                                             rot_p, P]
+    lib.pkv_paged_decode_noalloc.restype = I
     lib.pkv_status_string.argtypes = [I]
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.pkv_last_error.argtypes = []
