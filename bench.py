@@ -59,6 +59,9 @@ def parse():
                     help="time only the prefill legs (for profiling them alone)")
     ap.add_argument("--decode-large-only", action="store_true",
                     help="time only the large decode batch (for profiling it alone)")
+    ap.add_argument("--graph-only", action="store_true",
+                    help="only the launch-bound decode step, eager then replayed from a HIP "
+                         "graph, 1 ms apart (for a kernel trace of the two)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the graph-replay, rotary, mixed-step and large-batch legs")
     ap.add_argument("--cpu-seconds", type=float, default=6.0,
@@ -243,6 +246,39 @@ def small_decode_graph(torch, pkv, workloads, DeviceStep, args) -> dict:
     out = graph_step(torch, pkv, st, ws, args)
     out["workload"] = "4 seqs, ctx 150-400, 32 q / 32 kv heads, head_dim 128, block_size 256"
     del st
+    return out
+
+
+def graph_phases(torch, pkv, workloads, DeviceStep, args) -> dict:
+    """The launch-bound decode step run `steps` times eagerly, then replayed `steps` times
+    from a HIP graph, with a synchronisation and a 1 ms pause between the two phases so
+    a kernel trace separates them.  Reports the host's enqueue time and the elapsed
+    time per step of each phase."""
+    from paged_kv_cache_437_amd.graphs import DecodeStepGraph
+    from workloads import SeqSpec
+    ws = workloads.custom("decode_small_bf16", "bf16", 32, 32, 128, 256,
+                          [SeqSpec("decode", L, 1) for L in (200, 300, 150, 400)],
+                          seed=args.seed)
+    st = DeviceStep(ws, device="cuda", stale="nan")
+    g = DecodeStepGraph(st.k_cache, st.v_cache, ws.num_q_heads, len(st.plan.decode),
+                        st.decode_tables.shape[1], ws.scale)
+    g.run(st.q_decode, st.k_new, st.v_new, st.slot_mapping, st.decode_tables, st.context_lens)
+    for _ in range(args.warmup):
+        st.run()
+        g.graph.replay()
+    torch.cuda.synchronize()
+    out = {"workload": "4 seqs, ctx 150-400, 32 q / 32 kv heads, head_dim 128, block_size 256",
+           "steps": args.steps}
+    for mode, fn in (("eager", st.run), ("graph", g.graph.replay)):
+        time.sleep(0.001)
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            fn()
+        t1 = time.perf_counter()
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        out[mode] = {"host_enqueue_us_per_step": round(1e6 * (t1 - t0) / args.steps, 2),
+                     "elapsed_us_per_step": round(1e6 * (t2 - t0) / args.steps, 2)}
     return out
 
 
@@ -468,6 +504,10 @@ def main():
                "prefill_prefix_cached": prefill_leg(
                    torch, pkv, workloads.prefill_prefix_cached(seed=args.seed), DeviceStep, args)}
         print(json.dumps(out), flush=True)
+        return
+    if args.graph_only:
+        print(json.dumps({"graph_step": graph_phases(torch, pkv, workloads, DeviceStep, args)}),
+              flush=True)
         return
     if args.decode_large_only:
         print(json.dumps({"decode_large": decode_large_leg(torch, pkv, workloads, DeviceStep,
