@@ -152,27 +152,36 @@ def _quantiles(xs):
             "p90": float(np.percentile(a, 90)), "mean": float(a.mean()), "n": int(a.size)}
 
 
+WARM_S = 0.1  # least GPU-busy time of the untimed calls before a per-kernel figure
+
+
 def per_launch(torch, pkv, fn, reps, warmup=5, flush=None):
-    """The protocol of every per-kernel figure: `warmup` untimed calls, then `reps` calls
-    each timed on its own (the library's HIP events around each of its kernel launches,
-    on the launch's stream), with `flush()` before each call outside the timed region.
-    Returns {kernel name: quantiles of its per-launch milliseconds}."""
-    for _ in range(warmup):
-        if flush is not None:
-            flush()
-        fn()
-    torch.cuda.synchronize()
+    """The protocol of every per-kernel figure: untimed calls (at least `warmup`, and
+    for at least WARM_S seconds, so the timed launches run at the clocks of a busy GPU
+    rather than of one just out of host-side setup), then `reps` calls each timed on its
+    own (the library's HIP events around each of its kernel launches, on the launch's
+    stream), issued back to back with no synchronisation between them, with `flush()`
+    before each call outside the events.  Returns {kernel name: quantiles of its
+    per-launch milliseconds}."""
+    n, t0 = 0, time.perf_counter()
+    while n < warmup or time.perf_counter() - t0 < WARM_S:
+        for _ in range(warmup):
+            if flush is not None:
+                flush()
+            fn()
+        n += warmup
+        torch.cuda.synchronize()
     pkv.timing_collect()
-    samples = {}
     for _ in range(reps):
         if flush is not None:
             flush()
-        torch.cuda.synchronize()
         pkv.timing_enable(True)
         fn()
         pkv.timing_enable(False)
-        for name, t in pkv.timing_collect().items():
-            samples.setdefault(name, []).extend([t["total_ms"] / t["launches"]] * t["launches"])
+    torch.cuda.synchronize()
+    samples = {}
+    for name, ms in pkv.timing_samples(64 * reps):
+        samples.setdefault(name, []).append(ms)
     return {k: _quantiles(v) for k, v in samples.items()}
 
 
@@ -208,8 +217,9 @@ def decode_roofline(torch, pkv, step, d_bytes, args, flush):
             "algorithmic_bytes_per_launch": d_bytes,
             "launch_ms": {k: round(v, 5) for k, v in q[name].items() if k != "n"},
             "launches": q[name]["n"],
-            "protocol": f"5 warm-ups, {q[name]['n']} launches each timed alone, 512 MiB "
-                        "scratch written before each; median (p10/p90)",
+            "protocol": f"untimed calls for >= 0.1 s, then {q[name]['n']} launches back to back, each timed by "
+                        "its own HIP events, a 512 MiB scratch write before each outside the "
+                        "events; median (p10/p90)",
             "kernels_median_ms": {k: round(v["median"], 5) for k, v in q.items()}}
 
 

@@ -391,6 +391,18 @@ typedef struct {
 pkv_status pkv_timing_enable(int32_t on);
 int32_t pkv_timing_collect(pkv_kernel_timing* out, int32_t capacity);
 
+/* The same recorded launches one by one, in launch order: waits for their events,
+ * writes one entry per launch (up to `capacity`; the rest are dropped) and returns
+ * how many launches there were, or a negative pkv_status on a HIP error.  The events
+ * are consumed, as by pkv_timing_collect; call one or the other.  Lets a caller time
+ * consecutive launches individually without synchronising between them. */
+typedef struct {
+  char kernel[64];
+  double ms;
+} pkv_kernel_sample;
+
+int32_t pkv_timing_samples(pkv_kernel_sample* out, int32_t capacity);
+
 /* Static text for a status code. */
 const char* pkv_status_string(pkv_status status);
 

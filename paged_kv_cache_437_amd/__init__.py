@@ -30,7 +30,7 @@ from ._lib import PkvError
 
 __all__ = ["store_kvcache", "paged_prefill", "paged_decode", "paged_decode_workspace_size",
            "mixed_attention", "rotary_table", "PkvError", "version", "library_path", "timing_enable",
-           "timing_collect", "validate_store", "validate_prefill", "validate_decode",
+           "timing_collect", "timing_samples", "validate_store", "validate_prefill", "validate_decode",
            "contract_names", "debug_enable", "debug_enabled", "paged_decode_noalloc"]
 
 _DTYPES = {torch.float32: _lib.PKV_F32, torch.bfloat16: _lib.PKV_BF16}
@@ -62,6 +62,17 @@ def timing_collect() -> dict:
                                   "avg_ms": e.total_ms / max(e.launches, 1),
                                   "min_ms": e.min_ms, "max_ms": e.max_ms}
     return out
+
+
+def timing_samples(capacity: int = 4096) -> list:
+    """[(kernel name, ms)] of every launch recorded since the last collect, in launch
+    order (consumes them, as timing_collect does)."""
+    lib = _lib.load()
+    buf = (_lib.PkvKernelSample * capacity)()
+    n = lib.pkv_timing_samples(buf, capacity)
+    if n < 0:
+        _lib.check(n)
+    return [(e.kernel.decode(), e.ms) for e in buf[:min(n, capacity)]]
 
 
 def _cache_desc(k_cache: torch.Tensor, v_cache: torch.Tensor) -> _lib.PkvCache:

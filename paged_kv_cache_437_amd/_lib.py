@@ -20,7 +20,7 @@ EXPORTED = (
     "pkv_paged_decode", "pkv_status_string", "pkv_last_error", "pkv_version",
     "pkv_store_kvcache_rotary", "pkv_paged_prefill_rotary", "pkv_paged_decode_rotary",
     "pkv_mixed_attention",
-    "pkv_timing_enable", "pkv_timing_collect",
+    "pkv_timing_enable", "pkv_timing_collect", "pkv_timing_samples",
     "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_num_free", "pkv_bm_ref_count",
     "pkv_bm_add_sequence", "pkv_bm_remove_sequence", "pkv_bm_can_allocate", "pkv_bm_allocate",
     "pkv_bm_num_cached_tokens", "pkv_bm_num_tokens", "pkv_bm_can_append",
@@ -64,6 +64,13 @@ class PkvKernelTiming(ctypes.Structure):
         ("total_ms", ctypes.c_double),
         ("min_ms", ctypes.c_double),
         ("max_ms", ctypes.c_double),
+    ]
+
+
+class PkvKernelSample(ctypes.Structure):
+    _fields_ = [
+        ("kernel", ctypes.c_char * 64),
+        ("ms", ctypes.c_double),
     ]
 
 
@@ -120,6 +127,8 @@ def load() -> ctypes.CDLL:
     lib.pkv_timing_enable.restype = I
     lib.pkv_timing_collect.argtypes = [ctypes.POINTER(PkvKernelTiming), I]
     lib.pkv_timing_collect.restype = I
+    lib.pkv_timing_samples.argtypes = [ctypes.POINTER(PkvKernelSample), I]
+    lib.pkv_timing_samples.restype = I
     I64 = ctypes.c_int64
     for name, args in (
         ("pkv_bm_create", [I, I, P, ctypes.POINTER(P)]),

@@ -5,6 +5,7 @@
 #include <cstring>
 #include <mutex>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "../../include/pkv.h"
@@ -77,32 +78,29 @@ pkv_status pkv_timing_enable(int32_t on) {
   return PKV_OK;
 }
 
-int32_t pkv_timing_collect(pkv_kernel_timing* out, int32_t capacity) {
+}  // extern "C"
+
+namespace {
+
+// Waits for every recorded launch and returns (kernel, ms) in launch order; the events
+// go back to the spare list.  *status is set to PKV_ERR_HIP if an event failed (that
+// launch is dropped).
+std::vector<std::pair<const char*, float>> drain(int32_t* status) {
   std::vector<Pending> done;
   {
     std::lock_guard<std::mutex> lk(g_mu);
     done.swap(g_pending);
   }
-  std::vector<Total> totals;
-  int32_t status = 0;
+  std::vector<std::pair<const char*, float>> res;
+  res.reserve(done.size());
   for (const Pending& p : done) {
     float ms = 0.f;
     if (hipEventSynchronize(p.stop) != hipSuccess ||
         hipEventElapsedTime(&ms, p.start, p.stop) != hipSuccess) {
-      status = PKV_ERR_HIP;
+      *status = PKV_ERR_HIP;
       continue;
     }
-    Total* t = nullptr;
-    for (Total& x : totals)
-      if (std::strcmp(x.kernel, p.kernel) == 0) t = &x;
-    if (t == nullptr) {
-      totals.push_back({p.kernel, 0, 0.0, 1e300, 0.0});
-      t = &totals.back();
-    }
-    t->launches += 1;
-    t->total_ms += ms;
-    if (ms < t->min_ms) t->min_ms = ms;
-    if (ms > t->max_ms) t->max_ms = ms;
+    res.emplace_back(p.kernel, ms);
   }
   {
     std::lock_guard<std::mutex> lk(g_mu);
@@ -110,6 +108,29 @@ int32_t pkv_timing_collect(pkv_kernel_timing* out, int32_t capacity) {
       g_spare.push_back(p.start);
       g_spare.push_back(p.stop);
     }
+  }
+  return res;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t pkv_timing_collect(pkv_kernel_timing* out, int32_t capacity) {
+  int32_t status = 0;
+  std::vector<Total> totals;
+  for (const auto& [kernel, ms] : drain(&status)) {
+    Total* t = nullptr;
+    for (Total& x : totals)
+      if (std::strcmp(x.kernel, kernel) == 0) t = &x;
+    if (t == nullptr) {
+      totals.push_back({kernel, 0, 0.0, 1e300, 0.0});
+      t = &totals.back();
+    }
+    t->launches += 1;
+    t->total_ms += ms;
+    if (ms < t->min_ms) t->min_ms = ms;
+    if (ms > t->max_ms) t->max_ms = ms;
   }
   if (status != 0) return status;
   const int32_t n = static_cast<int32_t>(totals.size());
@@ -120,6 +141,19 @@ int32_t pkv_timing_collect(pkv_kernel_timing* out, int32_t capacity) {
     out[i].total_ms = totals[i].total_ms;
     out[i].min_ms = totals[i].min_ms;
     out[i].max_ms = totals[i].max_ms;
+  }
+  return n;
+}
+
+int32_t pkv_timing_samples(pkv_kernel_sample* out, int32_t capacity) {
+  int32_t status = 0;
+  const auto res = drain(&status);
+  if (status != 0) return status;
+  const int32_t n = static_cast<int32_t>(res.size());
+  for (int32_t i = 0; i < n && i < capacity && out != nullptr; ++i) {
+    std::strncpy(out[i].kernel, res[i].first, sizeof(out[i].kernel) - 1);
+    out[i].kernel[sizeof(out[i].kernel) - 1] = '\0';
+    out[i].ms = res[i].second;
   }
   return n;
 }
