@@ -304,10 +304,31 @@ __device__ __forceinline__ void prefill_workgroup(
   if (BIG_BLOCK && n_kv > 1) te_next = tile_block(1);
 
   // rotary: cosines and sines of this row's position for the elements this lane holds
-  // in k-steps ks < KS/2 (loaded first, independent of q)
+  // in k-steps ks < KS/2.  When the item's rows of the table (one per token of its q
+  // tile) fit in the second K/V buffers, which are free until tile 1 is fetched, the
+  // workgroup lands them there once with coalesced direct-to-LDS loads and every lane
+  // reads its values back (the q heads of a tile share the rows); each lane reading its
+  // own row from global memory instead touches 32 rows per load instruction.  Row r's
+  // 16-byte chunk c sits at chunk c ^ (r % 16), so 16 consecutive rows read one logical
+  // chunk from distinct banks.
   constexpr int KR = ROT ? KS / 2 : 1;
+  constexpr int TROW = D * 4;                              // bytes of one table row
+  constexpr bool STAGE = ROT && BM_TOK * TROW <= 2 * TB;  // q tiles of <= 64 tokens
   f32x4_t rc[KR][2], rs[KR][2];
-  if constexpr (ROT) {
+  if constexpr (STAGE) {
+    constexpr int CPT = TROW / 16;          // 16-byte chunks per table row
+    constexpr int RPI = 64 / CPT;           // rows per wavefront load instruction
+    constexpr int RH = TB / TROW;           // rows per LDS buffer
+    constexpr int NI = (BM_TOK + RPI - 1) / RPI;
+    const int pos0 = Lk - Lq + tok0;        // position of the tile's first token
+    for (int i = wave; i < NI; i += 4) {    // wavefront-uniform
+      const int r = i * RPI + lane / CPT;
+      const int c = (lane % CPT) ^ (r & 15);
+      const int64_t pos = min(max(pos0 + r, 0), max_position - 1);
+      char* dst = i * RPI < RH ? k_lds1 + i * RPI * TROW : v_lds1 + (i * RPI - RH) * TROW;
+      dma16_ptr(cos_sin + pos * D + 4 * c, lds_addr(dst));
+    }
+  } else if constexpr (ROT) {
     const float* cs =
         cos_sin + static_cast<int64_t>(min(max(diag, 0), max_position - 1)) * D + 8 * hi;
 #pragma unroll
@@ -328,6 +349,22 @@ __device__ __forceinline__ void prefill_workgroup(
       w = *reinterpret_cast<const u32x4_t*>(
           q + (static_cast<int64_t>(q_begin + tok) * Hq + hq) * D + ks * 16 + 8 * hi);
     qb[ks] = __builtin_bit_cast(bf16x8_t, w);
+  }
+  if constexpr (STAGE) {
+    // the table rows have landed (this wave's loads and everyone's, after the barrier)
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    __syncthreads();
+    constexpr int RH = TB / TROW;
+    const int r = R - head * BM_TOK;  // this lane's token within the tile
+    const char* row = r < RH ? k_lds1 + r * TROW : v_lds1 + (r - RH) * TROW;
+#pragma unroll
+    for (int ks = 0; ks < KR; ++ks)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int c = 4 * ks + 2 * hi + h2;  // chunk of elements ks*16 + 8*hi + 4*h2 ..
+        rc[ks][h2] = *reinterpret_cast<const f32x4_t*>(row + 16 * (c ^ (r & 15)));
+        rs[ks][h2] = *reinterpret_cast<const f32x4_t*>(row + 16 * ((c + D / 8) ^ (r & 15)));
+      }
   }
   if constexpr (ROT) {
     // element d of k-step ks (d = ks*16 + 8*hi + e) pairs with d + D/2, which this lane
