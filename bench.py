@@ -3,6 +3,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--reps R] [--seed S]
                     [--no-cpu-baseline] [--no-prefill] [--no-extras]
+                    [--prefill-only | --decode-large-only | --graph-only | --copy-calibration]
 
 A step is one pass of the hot path over one batch of synthetic input: the KV write of
 the batch's new tokens (one per sequence), then paged decode of the batch: a 7B-shaped
@@ -12,11 +13,12 @@ blocks, bf16 with fp32 accumulation.  All inputs are resident in device memory b
 the timed region; the K timed steps run back to back between two device
 synchronisations, and ``value`` is the step's algorithmic HBM bytes over that time.
 
-Per-kernel figures follow one protocol: W' = 5 untimed launches, then R (default 50)
-launches each timed on its own with HIP events recorded on the stream the kernel runs on
-(the library brackets its launches when timing is on), reported as the median with the
-10th and 90th percentiles.  Before every decode launch of that protocol a 512 MiB
-scratch buffer is written outside the timed region, so the 256 MB last-level cache
+Per-kernel figures follow one protocol: untimed launches for at least 0.1 s (the
+shader clock is low right after host-side setup), then R (default 50) launches issued
+back to back, each timed on its own with HIP events recorded on the stream the kernel
+runs on (the library brackets its launches when timing is on), reported as the median
+with the 10th and 90th percentiles.  Before every decode launch of that protocol a
+512 MiB scratch buffer is written outside the events, so the 256 MB last-level cache
 cannot serve K/V.  ``roofline`` is the decode kernel of the headline step; ``prefill``
 the varlen causal prefill (16 q / 8 kv heads, 16 prompts of length uniform on
 [128, 2048]) in TFLOP/s over the unmasked causal pairs; ``prefill_shapes`` the
