@@ -69,6 +69,14 @@ template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
 }
+// The same move with bound_ctrl set (every lane of these row patterns has a source, so
+// the value is the same): in `x + dpp_b(x)` the compiler folds the move into the add
+// (v_add_f32_dpp), which it does not do for dpp().
+template <int CTRL>
+__device__ __forceinline__ float dpp_b(float x) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
 __device__ __forceinline__ int64_t read_lane64(int64_t x, int lane) {
   const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(x), lane);
   const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(x >> 32), lane);
@@ -141,13 +149,24 @@ __device__ __forceinline__ float dot_piece(u32x4_t a, u32x4_t b) {
 }
 
 // Sum over the DCH lanes that hold one token's pieces (16 lanes = a DPP row at head_dim
-// 128, 8 lanes = half a row at 64); every one of them gets the sum.
-template <int DCH>
+// 128, 8 lanes = half a row at 64); every one of them gets the sum.  FUSED: each step
+// one v_add_f32_dpp instead of a DPP move and an add (with the nops between them).
+// Identical sums either way.  Fused, the decode with 8 or 16 q heads per kv head ran
+// 14-16% faster, 1 or 2 within noise, and 4 (the large lognormal batch) 2-3% slower,
+// all with bit-identical outputs; the kernels fuse from 8 q heads per stream up.
+template <int DCH, bool FUSED>
 __device__ __forceinline__ float piece_sum(float x) {
-  x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
-  x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
-  x += dpp<0x141>(x);  // row_half_mirror
-  if constexpr (DCH == 16) x += dpp<0x140>(x);  // row_mirror
+  if constexpr (FUSED) {
+    x += dpp_b<0xB1>(x);
+    x += dpp_b<0x4E>(x);
+    x += dpp_b<0x141>(x);
+    if constexpr (DCH == 16) x += dpp_b<0x140>(x);
+  } else {
+    x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+    x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+    x += dpp<0x141>(x);  // row_half_mirror
+    if constexpr (DCH == 16) x += dpp<0x140>(x);  // row_mirror
+  }
   return x;
 }
 
@@ -430,7 +449,7 @@ __device__ __forceinline__ void decode_workgroup(
       float mx = -INFINITY;
 #pragma unroll
       for (int it = 0; it < VIT; ++it) {
-        const float d = piece_sum<DCH>(dot_piece(qv[h], buf.k[it]));
+        const float d = piece_sum<DCH, (GP >= 8)>(dot_piece(qv[h], buf.k[it]));
         s[it] = (it * TPI + sub < valid) ? d * scale_log2 : -INFINITY;
         mx = fmaxf(mx, s[it]);
       }
