@@ -330,3 +330,29 @@ def test_output_rounding_is_nearest_even(pkv):
     want_pre = workloads.round_to_bf16_bits(ref["prefill"].astype(np.float32))
     assert np.array_equal(dec, want_dec), "decode output not rounded to nearest even"
     assert np.array_equal(pre, want_pre), "prefill output not rounded to nearest even"
+
+
+def test_prefill_longest_prompts(pkv):
+    """The longest prompts of the configured workloads and beyond: one causal prompt of
+    8192 tokens and a 512-token suffix over a 16384-token context (work items of 128 and
+    256 K/V tiles), 8 q / 2 kv heads, head_dim 128, block_size 256.  The oracle runs one
+    query row at a time on 160 sampled rows per sequence (the first and last rows, rows
+    at q-tile and block edges, the rest at random); all other rows must be finite."""
+    S = workloads.SeqSpec
+    wl = workloads.custom("long_prefill", "bf16", 8, 2, 128, 256,
+                          [S("prefill", 8192, 8192), S("prefill", 16384, 512)], seed=31)
+    st = _step(wl)
+    got = st.outputs_numpy()["prefill"]
+    torch.cuda.synchronize()
+    assert np.isfinite(got).all()
+    rng = np.random.default_rng(31)
+    off = 0
+    for i, seq in enumerate(wl.seqs):
+        Lq, Lk = seq.new_tokens, seq.context_len
+        edges = [0, 1, 31, 32, 63, 64, 255, 256, Lq // 2, Lq - 65, Lq - 64, Lq - 2, Lq - 1]
+        rows = sorted(set(edges) | set(rng.choice(Lq, 160 - len(edges), replace=False).tolist()))
+        want = np.stack([oracle.causal_attention(wl.q[i][r:r + 1], wl.k[i][:Lk - Lq + r + 1],
+                                                 wl.v[i][:Lk - Lq + r + 1], wl.scale)[0]
+                         for r in rows])
+        assert_close(got[off + np.array(rows)], want, wl.dtype, f"{wl.name} seq {i}")
+        off += Lq
