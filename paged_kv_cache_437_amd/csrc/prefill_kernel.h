@@ -29,7 +29,9 @@
 // 16-byte chunk swizzle that keeps both operand reads free of bank conflicts.  Keys
 // at or past Lk re-read the tile's last valid key (stale rows never enter; their
 // scores are masked), table entries past the last used block are never read, and
-// causal masking is applied only on tiles that cross the diagonal.
+// causal masking is applied only on tiles that cross the diagonal.  The output rows go
+// out through LDS: a lane holds 16-byte pieces of one row spread over head_dim, so each
+// wave stages its 32 rows in a free K/V buffer and stores them whole.
 // Work order: workgroups take the (sequence, kv head, q tile) items by level, the q
 // tile's distance from the end of the longest prompt, in groups of 4 levels, so the
 // longest causal tiles start first, the shortest run last, and the tiles of one
@@ -542,18 +544,49 @@ __device__ __forceinline__ void prefill_workgroup(
                                                      false, false);
     l = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
   }
-  if (row_valid) {
+  {
+    // staged in LDS, row-major with a 16-byte chunk swizzle (chunk c of row r at
+    // c ^ (r % (D/8))), so the stores below write whole rows: one instruction covers
+    // 64 / (D/8) rows of 2D contiguous bytes instead of 32 rows x 16 bytes.  The K/V
+    // buffers the last tile did not use are free: every wave has passed the barrier of
+    // tile n_kv - 1, so it is done with tile n_kv - 2's buffers, and nothing was
+    // fetched into them since.  Each wave takes its own 32 rows' share, so no barrier.
+    constexpr int CPO = D / 8;        // 16-byte chunks per output row
+    constexpr int RPO = 64 / CPO;     // rows per store instruction
+    constexpr int WB = 32 * D * 2;    // bytes of a wave's 32 rows (half a K or V buffer)
+    char* stage = (n_kv & 1) ? (wave < 2 ? k_lds1 : v_lds1) : (wave < 2 ? k_lds0 : v_lds0);
+    stage += (wave & 1) * WB;
     const float inv = 1.f / l;
-    uint16_t* orow = out + (static_cast<int64_t>(q_begin + tok) * Hq + hq) * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
+        // d = 32*dt + 8*r4 + 4*hi .. +4: chunk 4*dt + r4 of the row, its half hi
         u32x2_t w;
         w[0] = pack_bf16x2(o[dt][4 * r4] * inv, o[dt][4 * r4 + 1] * inv);
         w[1] = pack_bf16x2(o[dt][4 * r4 + 2] * inv, o[dt][4 * r4 + 3] * inv);
-        *reinterpret_cast<u32x2_t*>(orow + 32 * dt + 8 * r4 + 4 * hi) = w;
+        *reinterpret_cast<u32x2_t*>(stage + l32 * (2 * D) +
+                                    16 * ((4 * dt + r4) ^ (l32 & (CPO - 1))) + 8 * hi) = w;
       }
+    const int cl = lane % CPO;
+    u32x4_t rows[32 / RPO];  // every read first, so they overlap
+#pragma unroll
+    for (int i = 0; i < 32 / RPO; ++i) {
+      const int rr = i * RPO + lane / CPO;
+      rows[i] = *reinterpret_cast<const u32x4_t*>(stage + rr * (2 * D) +
+                                                  16 * (cl ^ (rr & (CPO - 1))));
+    }
+#pragma unroll
+    for (int i = 0; i < 32 / RPO; ++i) {
+      const int rr = i * RPO + lane / CPO;  // row of the wave
+      const u32x4_t v = rows[i];
+      const int Rw = 32 * wave + rr;
+      const int hd = Rw / BM_TOK;
+      const int tk = tok0 + (Rw - hd * BM_TOK);
+      if (hd < G && tk < Lq)
+        *reinterpret_cast<u32x4_t*>(
+            out + (static_cast<int64_t>(q_begin + tk) * Hq + kvh * G + hd) * D + 8 * cl) = v;
+    }
   }
 }
 
