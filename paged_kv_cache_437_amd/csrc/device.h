@@ -84,6 +84,21 @@ __device__ __forceinline__ int wave_sum_uniform(int x) {
          __builtin_amdgcn_readlane(x, 32) + __builtin_amdgcn_readlane(x, 48);
 }
 
+// Inclusive prefix sum over the wavefront's 64 lanes with DPP moves only (no LDS round
+// trips): within each row of 16 lanes by shifts of 1, 2, 4 and 8 (lanes shifted in from
+// outside the row read 0), then the last lane of row 0 is added to row 1 and that of
+// row 2 to row 3 (row_bcast:15), then the last lane of row 1 to rows 2 and 3
+// (row_bcast:31).  Lanes outside the selected rows get the move's old value, 0.
+__device__ __forceinline__ int wave_scan_inclusive(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return x;
+}
+
 // Row of token `pos` of a sequence for kv head `kvh`, as an element offset into a
 // [num_blocks][block_size][Hkv][D] cache.  64-bit: large pools exceed 2^31 elements.
 __device__ __forceinline__ int64_t token_row(int32_t block, int pos, int bs_log2, int Hkv,

@@ -121,12 +121,7 @@ __device__ bool prefill_item(int64_t i, int batch, int Hkv, int bm_tok, int max_
     const int n = tiles_of(c);
     const int cnt = below(n, y0 + R) - below(n, y0);  // this sequence's levels in the group
     const int w = cnt * Hkv;                 // and its items there
-    int incl = w;                            // inclusive scan over the wavefront
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int t = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += t;
-    }
+    const int incl = wave_scan_inclusive(w);  // inclusive scan over the wavefront
     const int total = __builtin_amdgcn_readlane(incl, 63);
     if (r < total) {
       // the first lane whose inclusive count passes r has w > 0: a real sequence
