@@ -542,7 +542,9 @@ __device__ __forceinline__ void prefill_workgroup(
   {
     // staged in LDS, row-major with a 16-byte chunk swizzle (chunk c of row r at
     // c ^ (r % (D/8))), so the stores below write whole rows: one instruction covers
-    // 64 / (D/8) rows of 2D contiguous bytes instead of 32 rows x 16 bytes.  The K/V
+    // 64 / (D/8) rows of 2D contiguous bytes instead of 32 rows x 16 bytes.  The stores
+    // are non-temporal: nothing here reads the output again, and the K/V tiles that the
+    // other q tiles of a sequence re-read keep the L2 to themselves.  The K/V
     // buffers the last tile did not use are free: every wave has passed the barrier of
     // tile n_kv - 1, so it is done with tile n_kv - 2's buffers, and nothing was
     // fetched into them since.  Each wave takes its own 32 rows' share, so no barrier.
@@ -579,8 +581,8 @@ __device__ __forceinline__ void prefill_workgroup(
       const int hd = Rw / BM_TOK;
       const int tk = tok0 + (Rw - hd * BM_TOK);
       if (hd < G && tk < Lq)
-        *reinterpret_cast<u32x4_t*>(
-            out + (static_cast<int64_t>(q_begin + tk) * Hq + kvh * G + hd) * D + 8 * cl) = v;
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(
+            out + (static_cast<int64_t>(q_begin + tk) * Hq + kvh * G + hd) * D + 8 * cl));
     }
   }
 }
