@@ -82,20 +82,26 @@ __device__ __forceinline__ int64_t read_lane64(int64_t x, int lane) {
   const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(x >> 32), lane);
   return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
 }
-__device__ __forceinline__ int64_t shfl_up64(int64_t x, int d) {
-  const int lo = __shfl_up(static_cast<int>(x), d, 64);
-  const int hi = __shfl_up(static_cast<int>(x >> 32), d, 64);
-  return static_cast<int64_t>((static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) |
-                              static_cast<uint32_t>(lo));
+// One DPP move of a 64-bit value (both halves moved alike; lanes without a source, or
+// outside the selected rows, get 0).
+template <int CTRL, int ROW_MASK, bool BC>
+__device__ __forceinline__ int64_t dpp64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(x), CTRL, ROW_MASK, 0xF, BC);
+  const uint32_t hi =
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(x >> 32), CTRL, ROW_MASK, 0xF, BC);
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
 }
-__device__ __forceinline__ int64_t wave_sum64(int64_t x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const int lo = __shfl_xor(static_cast<int>(x), o, 64);
-    const int hi = __shfl_xor(static_cast<int>(x >> 32), o, 64);
-    x += static_cast<int64_t>((static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) |
-                              static_cast<uint32_t>(lo));
-  }
+// Inclusive prefix sum over the wavefront's 64 lanes with DPP moves only (no LDS round
+// trips): within each row of 16 lanes by shifts of 1, 2, 4 and 8, then row 0's last
+// lane into row 1 and row 2's into row 3 (row_bcast:15), then row 1's last lane into
+// rows 2 and 3 (row_bcast:31).  Lane 63 ends with the wavefront's total.
+__device__ __forceinline__ int64_t wave_scan64(int64_t x) {
+  x += dpp64<0x111, 0xF, true>(x);   // row_shr:1
+  x += dpp64<0x112, 0xF, true>(x);   // row_shr:2
+  x += dpp64<0x114, 0xF, true>(x);   // row_shr:4
+  x += dpp64<0x118, 0xF, true>(x);   // row_shr:8
+  x += dpp64<0x142, 0xA, false>(x);  // row_bcast:15
+  x += dpp64<0x143, 0xC, false>(x);  // row_bcast:31
   return x;
 }
 
@@ -252,7 +258,7 @@ __device__ __forceinline__ void decode_workgroup(
   int64_t tot = 0;
   for (int b0 = 0; b0 < batch; b0 += 64)
     if (b0 + lane < batch) tot += static_cast<int64_t>(chunks_of(context_lens[b0 + lane], CH_LOG2)) * S;
-  const int64_t C = read_lane64(wave_sum64(tot), 0);
+  const int64_t C = read_lane64(wave_scan64(tot), 63);
   const int64_t W = num_workers;
   const int64_t c_begin = worker * C / W;
   const int64_t c_end = (worker + 1) * C / W;
@@ -263,12 +269,7 @@ __device__ __forceinline__ void decode_workgroup(
     for (int b0 = 0; b0 < batch; b0 += 64) {
       const int b = b0 + lane;
       const int64_t n = b < batch ? static_cast<int64_t>(chunks_of(context_lens[b], CH_LOG2)) * S : 0;
-      int64_t incl = n;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int64_t t = shfl_up64(incl, o);
-        if (lane >= o) incl += t;
-      }
+      const int64_t incl = wave_scan64(n);
       const int64_t excl = carry + incl - n;
       if (worker == 0 && b < batch) ws_prefix[b] = excl;
       if (b_first < 0) {
