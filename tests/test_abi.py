@@ -20,7 +20,8 @@ def lib():
 
 
 def declared_functions():
-    text = open(os.path.join(ROOT, "include", "pkv.h")).read()
+    with open(os.path.join(ROOT, "include", "pkv.h")) as f:
+        text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", text)))
 

@@ -135,7 +135,10 @@ def test_mutant_is_caught(name, monkeypatch):
     caught = []
     for pin in ALL_PINS:
         try:
-            pin()
+            # a planted mistake may read the NaN-poisoned stale blocks: numpy's warning
+            # about it is expected here, the pins' verdict is what counts
+            with np.errstate(invalid="ignore"):
+                pin()
         except (AssertionError, ValueError, IndexError, KeyError, RuntimeError, TypeError):
             caught.append(pin.__name__)
     assert caught, f"no pin catches the planted mistake {name!r}"
