@@ -585,6 +585,17 @@ def main():
         result["rotary"] = {"decode_ms_per_step": round(r_ms / args.steps, 5),
                             "plain_decode_ms_per_step": round(e_ms / args.steps, 5)}
         del rstep
+        # the same step through pkv_paged_decode_append: the decode kernel writes the new
+        # tokens' rows itself (one launch fewer), same bits
+        for _ in range(args.warmup):
+            step.run_appended()
+        a_ms, _ = timed_steps(torch, pkv, step.run_appended, args.steps)
+        e_ms, _ = timed_steps(torch, pkv, step.run, args.steps)
+        result["appended_step"] = {
+            "what": "KV write + decode in one call (pkv_paged_decode_append) against the two "
+                    "calls, one after the other in the same run",
+            "ms_per_step": round(a_ms / args.steps, 5),
+            "separate_ms_per_step": round(e_ms / args.steps, 5)}
     del step
     torch.cuda.empty_cache()
 

@@ -199,6 +199,29 @@ pkv_status pkv_paged_decode_rotary(const pkv_cache* cache, const void* q, void* 
                                    int32_t num_workers, const pkv_rotary* rotary,
                                    hipStream_t stream);
 
+/* One decode step in one call: the KV write of each sequence's new token and the
+ * decode over the context that now ends with it (“深入 Nano-vLLM 推理引擎”, "Prefill and
+ * Decode": a decode step appends one token per sequence and attends over the whole
+ * context).  k_new, v_new: [batch][num_kv_heads][head_dim] device arrays of the cache's
+ * element type, the new token of each sequence; slot_mapping: int32 [batch] on the
+ * device, the cache slot of position context_lens[b] - 1 of sequence b (the slot
+ * pkv_store_kvcache would be given), -1 to skip the write.  The other arguments are
+ * those of pkv_paged_decode.  The cache and out end bit-identical to pkv_store_kvcache
+ * (k_new, v_new, slot_mapping, batch tokens) followed by pkv_paged_decode with the same
+ * num_workers, provided slot_mapping[b] is that slot of block_tables[b] (with -1 the
+ * cache row is left alone while the attention may still take the token from k_new /
+ * v_new).  With bf16 caches, one q head per kv head and blocks of at least one decode
+ * chunk (8 tokens at head_dim 128) the decode kernel writes the new rows itself and
+ * takes the new token's K and V from k_new / v_new, saving the KV-write launch;
+ * otherwise the two kernels run in turn.  Errors as in the two calls. */
+pkv_status pkv_paged_decode_append(const pkv_cache* cache, const void* q, const void* k_new,
+                                   const void* v_new, void* out, int32_t num_q_heads,
+                                   int32_t batch, const int32_t* slot_mapping,
+                                   const int32_t* context_lens, int32_t max_context_len,
+                                   const int32_t* block_tables, int32_t block_table_stride,
+                                   float scale, void* workspace, size_t workspace_bytes,
+                                   int32_t num_workers, hipStream_t stream);
+
 /* pkv_paged_decode (or pkv_paged_decode_rotary when rotary is not NULL) without a
  * workspace argument, for callers that cannot allocate device memory: code under HIP
  * graph capture, tight serving loops, harnesses that forbid allocation.  The split-K

@@ -31,7 +31,8 @@ from ._lib import PkvError
 __all__ = ["store_kvcache", "paged_prefill", "paged_decode", "paged_decode_workspace_size",
            "mixed_attention", "rotary_table", "PkvError", "version", "library_path", "timing_enable",
            "timing_collect", "timing_samples", "validate_store", "validate_prefill", "validate_decode",
-           "contract_names", "debug_enable", "debug_enabled", "paged_decode_noalloc"]
+           "contract_names", "debug_enable", "debug_enabled", "paged_decode_noalloc",
+           "paged_decode_append"]
 
 _DTYPES = {torch.float32: _lib.PKV_F32, torch.bfloat16: _lib.PKV_BF16}
 
@@ -219,6 +220,50 @@ def paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     else:
         _lib.check(lib.pkv_paged_decode_rotary(ctypes.byref(desc), *args, ctypes.byref(rot),
                                                _stream(k_cache.device)))
+    return out
+
+
+def paged_decode_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                        k_cache: torch.Tensor, v_cache: torch.Tensor, slot_mapping: torch.Tensor,
+                        block_tables: torch.Tensor, context_lens: torch.Tensor,
+                        max_context_len: int, scale: float, num_workers: int = 0,
+                        out: torch.Tensor | None = None,
+                        workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """One decode step in one call: k_new, v_new [B, Hkv, D] (each sequence's new token)
+    go into the caches at slot_mapping [B] (the slot of position context_len - 1), and
+    q [B, Hq, D] attends over the contexts that end with them.  Same bits as
+    store_kvcache followed by paged_decode; one kernel (and the split merge) for bf16
+    caches with one q head per kv head and blocks of at least one decode chunk, the
+    two calls in turn otherwise."""
+    lib = _lib.load()
+    desc = _cache_desc(k_cache, v_cache)
+    if q.dim() != 3 or q.shape[2] != k_cache.shape[3]:
+        raise ValueError("q must be [B, Hq, D]")
+    batch = q.shape[0]
+    if context_lens.numel() != batch or block_tables.dim() != 2 or block_tables.shape[0] != batch:
+        raise ValueError("context_lens / block_tables disagree with q on batch")
+    if k_new.shape != (batch,) + tuple(k_cache.shape[2:]) or v_new.shape != k_new.shape:
+        raise ValueError(f"k_new, v_new must be [{batch}, Hkv, D] like the cache rows")
+    if slot_mapping.numel() != batch:
+        raise ValueError("slot_mapping must hold one slot per sequence")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    need = lib.pkv_paged_decode_workspace_size(ctypes.byref(desc), q.shape[1], batch,
+                                               int(max_context_len), int(num_workers))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _lib.check(lib.pkv_paged_decode_append(
+        ctypes.byref(desc), _dev(q, "q", k_cache.dtype, k_cache),
+        _dev(k_new, "k_new", k_cache.dtype, k_cache), _dev(v_new, "v_new", k_cache.dtype, k_cache),
+        _dev(out, "out", k_cache.dtype, k_cache), q.shape[1], batch,
+        _dev(slot_mapping, "slot_mapping", torch.int32, k_cache),
+        _dev(context_lens, "context_lens", torch.int32, k_cache), int(max_context_len),
+        _dev(block_tables, "block_tables", torch.int32, k_cache), block_tables.shape[1],
+        float(scale), ws_ptr, ws_bytes, int(num_workers), _stream(k_cache.device)))
     return out
 
 

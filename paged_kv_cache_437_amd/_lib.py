@@ -26,7 +26,7 @@ EXPORTED = (
     "pkv_bm_num_cached_tokens", "pkv_bm_num_tokens", "pkv_bm_can_append",
     "pkv_bm_append_token", "pkv_bm_deallocate", "pkv_bm_block_table",
     "pkv_validate_store", "pkv_validate_prefill", "pkv_validate_decode", "pkv_debug_enable",
-    "pkv_debug_enabled", "pkv_paged_decode_noalloc",
+    "pkv_debug_enabled", "pkv_paged_decode_noalloc", "pkv_paged_decode_append",
 )
 
 # contract bits of pkv_validate_* (include/pkv.h)
@@ -102,6 +102,9 @@ def load() -> ctypes.CDLL:
     lib.pkv_paged_decode.argtypes = [cache_p, P, P, I, I, P, I, P, I, ctypes.c_float, P,
                                      ctypes.c_size_t, I, P]
     lib.pkv_paged_decode.restype = I
+    lib.pkv_paged_decode_append.argtypes = [cache_p, P, P, P, P, I, I, P, P, I, P, I,
+                                            ctypes.c_float, P, ctypes.c_size_t, I, P]
+    lib.pkv_paged_decode_append.restype = I
     rot_p = ctypes.POINTER(PkvRotary)
     lib.pkv_store_kvcache_rotary.argtypes = [cache_p, P, P, P, P, I, rot_p, P]
     lib.pkv_store_kvcache_rotary.restype = I

@@ -323,6 +323,40 @@ pkv_status pkv_paged_decode_rotary(const pkv_cache* cache, const void* q, void* 
                      num_workers, rotary, stream);
 }
 
+pkv_status pkv_paged_decode_append(const pkv_cache* cache, const void* q, const void* k_new,
+                                   const void* v_new, void* out, int32_t num_q_heads,
+                                   int32_t batch, const int32_t* slot_mapping,
+                                   const int32_t* context_lens, int32_t max_context_len,
+                                   const int32_t* block_tables, int32_t block_table_stride,
+                                   float scale, void* workspace, size_t workspace_bytes,
+                                   int32_t num_workers, hipStream_t stream) {
+  pkv_status st = decode_impl(cache, q, out, num_q_heads, batch, context_lens, max_context_len,
+                              block_tables, block_table_stride, scale, workspace,
+                              workspace_bytes, num_workers, nullptr, stream, true);
+  if (st != PKV_OK || batch == 0) return st;
+  if (k_new == nullptr || v_new == nullptr || slot_mapping == nullptr)
+    return fail(PKV_ERR_INVALID, "k_new, v_new or slot_mapping is NULL");
+  if (cache->dtype == PKV_BF16) {
+    if (pkv::debug_checks_on() &&
+        ((st = pkv_validate_store(cache, slot_mapping, batch, 0, nullptr, stream)) != PKV_OK ||
+         (st = pkv_validate_decode(cache, batch, context_lens, max_context_len, block_tables,
+                                   block_table_stride, 0, nullptr, stream)) != PKV_OK))
+      return st;
+    const hipError_t e = pkv::launch_paged_decode_append_bf16(
+        cache->head_dim, q, out, cache->k_cache, cache->v_cache, num_q_heads,
+        cache->num_kv_heads, log2_exact(cache->block_size), batch, context_lens, block_tables,
+        block_table_stride, scale, num_workers, workspace, k_new, v_new, slot_mapping, stream);
+    if (e != hipErrorNotSupported) return launched(e, "paged_decode_append");
+  }
+  // grouped heads, blocks shorter than a decode chunk, or an fp32 cache: the two kernels
+  // in turn
+  if ((st = pkv_store_kvcache(cache, k_new, v_new, slot_mapping, batch, stream)) != PKV_OK)
+    return st;
+  return pkv_paged_decode(cache, q, out, num_q_heads, batch, context_lens, max_context_len,
+                          block_tables, block_table_stride, scale, workspace, workspace_bytes,
+                          num_workers, stream);
+}
+
 }  // extern "C"
 
 pkv_status pkv_mixed_attention(const pkv_cache* cache, int32_t num_q_heads, float scale,

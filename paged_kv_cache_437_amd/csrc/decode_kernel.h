@@ -139,6 +139,15 @@ struct KVBuf {
   u32x4_t v[kChunkLoads];
 };
 
+// The step's new token of every sequence, for a decode that appends it itself:
+// k_new / v_new [batch][Hkv][D], and slots[b], the cache slot of position
+// context_lens[b] - 1 (where a separate KV write would have put it; -1: not written).
+struct DecodeAppend {
+  const uint16_t* k_new = nullptr;
+  const uint16_t* v_new = nullptr;
+  const int32_t* slots = nullptr;
+};
+
 // q . k over one 16-byte piece (8 products as 4 bf16 pair dot products, fp32
 // accumulation)
 __device__ __forceinline__ float dot_piece(u32x4_t a, u32x4_t b) {
@@ -215,7 +224,7 @@ __device__ __forceinline__ float sub_sum(float x) {
 
 // One workgroup (four wavefront workers, wg*4 .. wg*4+3) of the decode pass; the
 // kernels that run it give it its index.
-template <int D, int GP, int MH, bool ONE_BLOCK, bool ROT>
+template <int D, int GP, int MH, bool ONE_BLOCK, bool ROT, bool APPEND = false>
 __device__ __forceinline__ void decode_workgroup(
     int wg, const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
     const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
@@ -223,8 +232,9 @@ __device__ __forceinline__ void decode_workgroup(
     int table_stride, int batch, int Hq, int Hkv, int G, int n_hg, int bs_log2,
     float scale_log2, int num_workers, int64_t* __restrict__ ws_prefix,
     float2* __restrict__ ws_ml, float* __restrict__ ws_o, const float* __restrict__ cos_sin,
-    int max_position) {
+    int max_position, DecodeAppend app = {}) {
   static_assert(D == 64 || D == 128, "head_dim");
+  static_assert(!APPEND || (ONE_BLOCK && !ROT), "appending decode: chunks in one block, no rotary");
   static_assert(GP == 1 || GP == 2 || GP == 4 || GP == 8, "q heads per kv head in a stream");
   constexpr int DCH = D / 8;         // 16-byte pieces per head row
   constexpr int HPI = 64 / DCH;      // head rows per load instruction
@@ -337,16 +347,30 @@ __device__ __forceinline__ void decode_workgroup(
   for (int it = 0; it < VIT; ++it)
     kv_off[it] = static_cast<uint32_t>(it * TPI + sub) * row_bytes + hh * D * 2 + piece * 16;
   const uint32_t q_off = static_cast<uint32_t>(hh * G * D * 2 + piece * 16);
+  // this lane's piece of kv head kv0 + hh in a row of k_new / v_new
+  const uint32_t kn_off = static_cast<uint32_t>(hh * D * 2 + piece * 16);
   // this lane's pieces of the q rows of x's stream (kv head hh, q heads g < GP; rows
   // past the group's heads re-read its last one, and those heads are never written
   // out).  Loaded once per segment, in order between the loads of its first chunk
   // and those of the chunk after, so the wait for them is the wait for that chunk.
   u32x4_t qv[GP];
+  u32x4_t kn, vn;  // appending decode: this lane's pieces of the stream's new token
   auto load_q = [&](const Cursor& x) {
     const int kvg = n_hg == 1 ? x.j : x.j / n_hg;
     const int hg = x.j - kvg * n_hg;
     const int nh = min(GP, G - hg * GP);
     const int qrow0 = kvg * MH * G + hg * GP;  // this lane's q rows: qrow0 + hh*G + g
+    if constexpr (APPEND) {
+      // the stream's new token (its kv heads' rows of k_new / v_new), with q: once per
+      // segment, used by the stream's last chunk and written out at its end
+      const int64_t nrow = (static_cast<int64_t>(x.b) * Hkv + kvg * MH) * D;
+      const auto knr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(app.k_new + nrow),
+                                                         0, MH * D * 2, kBufferWord3);
+      const auto vnr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(app.v_new + nrow),
+                                                         0, MH * D * 2, kBufferWord3);
+      kn = __builtin_amdgcn_raw_buffer_load_b128(knr, kn_off, 0, 0);
+      vn = __builtin_amdgcn_raw_buffer_load_b128(vnr, kn_off, 0, 0);
+    }
     if constexpr (ONE_BLOCK) {
       const auto qr = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<uint16_t*>(q + static_cast<int64_t>(x.b) * Hq * D), 0, Hq * D * 2,
@@ -393,7 +417,11 @@ __device__ __forceinline__ void decode_workgroup(
       (void)live;
       const int64_t blk = __builtin_amdgcn_readfirstlane(te);
       const int64_t first = ((blk << bs_log2) | (tok0 & bs_mask)) * Hkv + kv0;
-      const int bytes = (min(x.L - tok0, CH) - 1) * static_cast<int>(row_bytes) + MH * D * 2;
+      // an appending decode takes the stream's last row (the new token) from k_new /
+      // v_new: the descriptor of its last chunk ends before that row
+      const bool new_row = APPEND && x.k == x.nch - 1;
+      const int bytes = (min(x.L - tok0, CH) - 1) * static_cast<int>(row_bytes) +
+                        (new_row ? 0 : MH * D * 2);
       const auto kr = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<uint16_t*>(k_cache + first * D), 0, bytes, kBufferWord3);
       const auto vr = __builtin_amdgcn_make_buffer_rsrc(
@@ -495,6 +523,18 @@ __device__ __forceinline__ void decode_workgroup(
     const int kvg = n_hg == 1 ? x.j : x.j / n_hg;
     const int hg = x.j - kvg * n_hg;
     const int nh = min(GP, G - hg * GP);
+    if constexpr (APPEND) {
+      // the stream's last chunk ran here: its first q-head group writes the new token's
+      // rows of these kv heads into the cache (no chunk of this launch reads them)
+      if (x.k == x.nch - 1 && hg == 0) {
+        const int32_t slot = app.slots[x.b];
+        if (slot >= 0 && sub == 0) {
+          const int64_t row = (static_cast<int64_t>(slot) * Hkv + kvg * MH + hh) * D + piece * 8;
+          *reinterpret_cast<u32x4_t*>(const_cast<uint16_t*>(k_cache) + row) = kn;
+          *reinterpret_cast<u32x4_t*>(const_cast<uint16_t*>(v_cache) + row) = vn;
+        }
+      }
+    }
     // sum the shares of the lanes holding the same head and head_dim piece
     float l_h[GP];
 #pragma unroll
@@ -564,6 +604,20 @@ __device__ __forceinline__ void decode_workgroup(
     issue(nxt, te_nxt, Y, has_next);
     // keep those loads here, ahead of the computation of the current chunk
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (APPEND) {
+      // a stream's last chunk: the context's last row is the new token, whose pieces
+      // come from k_new / v_new (the chunk's descriptor ends before that row).  X is
+      // this half-step's own buffer, so the substitution is in place.
+      if (cur.k == cur.nch - 1) {
+        const int valid = cur.L - cur.k * CH;
+#pragma unroll
+        for (int it = 0; it < VIT; ++it)
+          if (it * TPI + sub == valid - 1) {
+            X.k[it] = kn;
+            X.v[it] = vn;
+          }
+      }
+    }
     accumulate(cur, X);
     if (!has_next || cur.k == cur.nch - 1) return true;
     ++i;

@@ -49,6 +49,22 @@ hipError_t launch_paged_decode_bf16(int head_dim, const void* q, void* out, cons
                                     int num_workers, void* workspace, const float* cos_sin,
                                     int max_position, hipStream_t stream);
 
+// launch_paged_decode_bf16 (no rotary) that also appends the step's new token of each
+// sequence: k_new / v_new [batch][num_kv_heads][head_dim] go into the cache at
+// slot_mapping[b] (the slot of position context_lens[b] - 1; -1 skips the write), and the
+// attention takes that token from k_new / v_new; cache and output bits are those of
+// launch_store_kvcache followed by launch_paged_decode_bf16.  Returns
+// hipErrorNotSupported for grouped heads (num_q_heads != num_kv_heads) or when a chunk
+// would span blocks; the caller then launches both.
+hipError_t launch_paged_decode_append_bf16(int head_dim, const void* q, void* out,
+                                           const void* k_cache, const void* v_cache,
+                                           int num_q_heads, int num_kv_heads, int bs_log2,
+                                           int batch, const int32_t* context_lens,
+                                           const int32_t* block_tables, int table_stride,
+                                           float scale, int num_workers, void* workspace,
+                                           const void* k_new, const void* v_new,
+                                           const int32_t* slot_mapping, hipStream_t stream);
+
 // The worker count the bf16 decode picks when asked for 0 (auto).
 int paged_decode_bf16_workers(int head_dim, int num_q_heads, int num_kv_heads, int bs_log2);
 

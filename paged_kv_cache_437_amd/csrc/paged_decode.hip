@@ -23,7 +23,52 @@ paged_decode_bf16_kernel(
       max_position);
 }
 
+// The same pass appending the step's new token of each sequence itself (chunks in one
+// block, no rotary): the cache rows of the new tokens are written by the kernel, and the
+// token's K and V enter the attention from k_new / v_new.
+template <int D, int GP, int MH>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void
+paged_decode_append_bf16_kernel(
+    const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
+    const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
+    const int32_t* __restrict__ context_lens, const int32_t* __restrict__ block_tables,
+    int table_stride, int batch, int Hq, int Hkv, int G, int n_hg, int bs_log2,
+    float scale_log2, int num_workers, int64_t* __restrict__ ws_prefix,
+    float2* __restrict__ ws_ml, float* __restrict__ ws_o, DecodeAppend app) {
+  decode_workgroup<D, GP, MH, true, false, true>(
+      blockIdx.x, q, out, k_cache, v_cache, context_lens, block_tables, table_stride, batch, Hq,
+      Hkv, G, n_hg, bs_log2, scale_log2, num_workers, ws_prefix, ws_ml, ws_o, nullptr, 0, app);
+}
+
 namespace {
+
+template <int D, int GP, int MH>
+hipError_t launch_decode_append(const void* q, void* out, const void* k_cache,
+                                const void* v_cache, int num_q_heads, int num_kv_heads,
+                                int bs_log2, int batch, const int32_t* context_lens,
+                                const int32_t* block_tables, int table_stride, float scale,
+                                int num_workers, void* workspace, const DecodeAppend& app,
+                                hipStream_t stream) {
+  if ((1 << bs_log2) < chunk_tokens(D, MH)) return hipErrorNotSupported;
+  const int G = num_q_heads / num_kv_heads;
+  const int n_hg = (G + GP - 1) / GP;
+  const int S = (num_kv_heads / MH) * n_hg;
+  if (S > 65535) return hipErrorInvalidConfiguration;
+  const int W = num_workers > 0 ? num_workers : auto_decode_workers(GP);
+  const DecodeWorkspace ws = carve_decode_workspace(workspace, batch, W, MH * GP);
+  const float scale_log2 = scale * kLog2e;
+  timing_begin("paged_decode_append", stream);
+  hipLaunchKernelGGL((paged_decode_append_bf16_kernel<D, GP, MH>), dim3((W + 3) / 4), dim3(256),
+                     0, stream, static_cast<const uint16_t*>(q), static_cast<uint16_t*>(out),
+                     static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache),
+                     context_lens, block_tables, table_stride, batch, num_q_heads, num_kv_heads, G,
+                     n_hg, bs_log2, scale_log2, W, ws.prefix, ws.ml, ws.o, app);
+  timing_end(stream);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_decode_combine(D, GP, MH, ws, out, context_lens, batch, num_q_heads,
+                               num_kv_heads, W, stream);
+}
 
 template <int D, int GP, int MH, bool ONE_BLOCK>
 hipError_t launch_decode(const void* q, void* out, const void* k_cache, const void* v_cache,
@@ -134,6 +179,40 @@ hipError_t launch_paged_decode_bf16(int head_dim, const void* q, void* out, cons
     case 2: PKV_DEC(64, 2);
     case 4: PKV_DEC(64, 4);
     default: PKV_DEC(64, 8);
+  }
+#undef PKV_DEC
+}
+
+hipError_t launch_paged_decode_append_bf16(int head_dim, const void* q, void* out,
+                                           const void* k_cache, const void* v_cache,
+                                           int num_q_heads, int num_kv_heads, int bs_log2,
+                                           int batch, const int32_t* context_lens,
+                                           const int32_t* block_tables, int table_stride,
+                                           float scale, int num_workers, void* workspace,
+                                           const void* k_new, const void* v_new,
+                                           const int32_t* slot_mapping, hipStream_t stream) {
+  // one q head per kv head only: with grouped heads the appending kernel measured slower
+  // than the KV write and the plain decode together
+  if (num_q_heads != num_kv_heads) return hipErrorNotSupported;
+  const int MH = kv_heads_per_stream(head_dim, num_kv_heads, 1);
+  DecodeAppend app;
+  app.k_new = static_cast<const uint16_t*>(k_new);
+  app.v_new = static_cast<const uint16_t*>(v_new);
+  app.slots = slot_mapping;
+#define PKV_DEC(D_, MH_)                                                                      \
+  return launch_decode_append<D_, 1, MH_>(q, out, k_cache, v_cache, num_q_heads, num_kv_heads, \
+                                          bs_log2, batch, context_lens, block_tables,          \
+                                          table_stride, scale, num_workers, workspace, app,    \
+                                          stream)
+  // with one q head per kv head a stream holds at most 512 bytes of kv-head rows
+  if (head_dim == 128) {
+    if (MH == 1) PKV_DEC(128, 1);
+    PKV_DEC(128, 2);
+  }
+  switch (MH) {
+    case 1: PKV_DEC(64, 1);
+    case 2: PKV_DEC(64, 2);
+    default: PKV_DEC(64, 4);
   }
 #undef PKV_DEC
 }

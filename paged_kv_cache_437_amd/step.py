@@ -13,7 +13,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (contract_names, mixed_attention, paged_decode, paged_decode_workspace_size,
+from . import (contract_names, mixed_attention, paged_decode, paged_decode_append,
+               paged_decode_workspace_size,
                paged_prefill, store_kvcache, validate_decode, validate_prefill, validate_store)
 from .control import BlockPool, plan_step
 
@@ -113,6 +114,7 @@ class DeviceStep:
         self.positions = i32(p.step_pos)
 
         self.q_prefill = self.q_decode = None
+        self._append_rows = None
         if p.prefill:
             self.q_prefill = to_device_values(np.concatenate([wl.q[i] for i in p.prefill]), dev)
             self.cu_seqlens_q = i32(p.cu_seqlens_q)
@@ -155,6 +157,32 @@ class DeviceStep:
         self.store()
         self.prefill()
         self.decode()
+        return self
+
+    def decode_append(self):
+        """A decode-only step in one call: the decode sequences' new tokens are written
+        by the decode itself (paged_decode_append; same bits as store() + decode())."""
+        if self.q_decode is None:
+            return None
+        if self.q_prefill is not None or self.rotary is not None:
+            raise ValueError("decode_append covers decode-only steps without rotary")
+        p = self.plan
+        if self._append_rows is None:
+            where = {int(s): t for t, s in enumerate(p.step_seq)}
+            idx = torch.tensor([where[i] for i in p.decode], dtype=torch.long,
+                               device=self.device)
+            self._append_rows = (self.k_new.index_select(0, idx).contiguous(),
+                                 self.v_new.index_select(0, idx).contiguous(),
+                                 self.slot_mapping.index_select(0, idx).contiguous())
+        k_new, v_new, slots = self._append_rows
+        return paged_decode_append(self.q_decode, k_new, v_new, self.k_cache, self.v_cache,
+                                   slots, self.decode_tables, self.context_lens,
+                                   p.max_context_len, self.wl.scale,
+                                   num_workers=self.num_workers, out=self.out_decode,
+                                   workspace=self.workspace)
+
+    def run_appended(self):
+        self.decode_append()
         return self
 
     def mixed(self):
