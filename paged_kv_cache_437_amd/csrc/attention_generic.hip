@@ -124,10 +124,11 @@ static void launch_one(const void* q, void* out, const void* kc, const void* vc,
                        hipStream_t stream) {
   dim3 grid((max_q_rows + 3) / 4, batch, Hq);
   timing_begin(ctx != nullptr ? "attention_generic_decode" : "attention_generic_prefill", stream);
-  hipLaunchKernelGGL((attention_generic_kernel<T, D>), grid, dim3(256), 0, stream,
-                     static_cast<const T*>(q), static_cast<T*>(out), static_cast<const T*>(kc),
-                     static_cast<const T*>(vc), Hq, Hkv, bs_log2, cu_q, cu_k, ctx, tables, stride,
-                     scale_log2, cos_sin, max_position);
+  hipExtLaunchKernelGGL((attention_generic_kernel<T, D>), grid, dim3(256), 0, stream,
+                        timing_start(), timing_stop(), 0, static_cast<const T*>(q),
+                        static_cast<T*>(out), static_cast<const T*>(kc), static_cast<const T*>(vc),
+                        Hq, Hkv, bs_log2, cu_q, cu_k, ctx, tables, stride, scale_log2, cos_sin,
+                        max_position);
   timing_end(stream);
 }
 

@@ -115,13 +115,13 @@ hipError_t launch_decode_combine(int head_dim, int GP, int MH, const DecodeWorks
   uint16_t* o = static_cast<uint16_t*>(out);
   timing_begin("paged_decode_combine", stream);
   if (head_dim == 128)
-    hipLaunchKernelGGL((decode_combine_kernel<128>), grid, dim3(128), 0, stream, ws.prefix,
-                       ws.ml, ws.o, o, context_lens, batch, num_q_heads, G, GP, MH, n_hg,
-                       ch_log2, num_workers);
+    hipExtLaunchKernelGGL((decode_combine_kernel<128>), grid, dim3(128), 0, stream, timing_start(),
+                          timing_stop(), 0, ws.prefix, ws.ml, ws.o, o, context_lens, batch,
+                          num_q_heads, G, GP, MH, n_hg, ch_log2, num_workers);
   else
-    hipLaunchKernelGGL((decode_combine_kernel<64>), grid, dim3(64), 0, stream, ws.prefix, ws.ml,
-                       ws.o, o, context_lens, batch, num_q_heads, G, GP, MH, n_hg, ch_log2,
-                       num_workers);
+    hipExtLaunchKernelGGL((decode_combine_kernel<64>), grid, dim3(64), 0, stream, timing_start(),
+                          timing_stop(), 0, ws.prefix, ws.ml, ws.o, o, context_lens, batch,
+                          num_q_heads, G, GP, MH, n_hg, ch_log2, num_workers);
   timing_end(stream);
   return hipGetLastError();
 }

@@ -69,15 +69,17 @@ hipError_t launch_mixed_attention_bf16(
   const dim3 grid(static_cast<unsigned>(slots + n_decode_wg));
   const float scale_log2 = scale * kLog2e;
 #define PKV_MIXED(D_, GP_, PGP_, MH_, ROT_)                                                    \
-  hipLaunchKernelGGL((mixed_attention_bf16_kernel<D_, GP_, PGP_, MH_, ROT_>), grid, dim3(256), 0, \
-                     stream, static_cast<const uint16_t*>(k_cache),                           \
-                     static_cast<const uint16_t*>(v_cache), num_q_heads, num_kv_heads, G,     \
-                     bs_log2, scale_log2, cos_sin, max_position, n_decode_wg,                 \
-                     static_cast<const uint16_t*>(q_decode), static_cast<uint16_t*>(out_decode), \
-                     context_lens, decode_tables, decode_stride, decode_batch, n_hg, W,       \
-                     ws.prefix, ws.ml, ws.o, static_cast<const uint16_t*>(q_prefill),         \
-                     static_cast<uint16_t*>(out_prefill), cu_seqlens_q, cu_seqlens_k,         \
-                     prefill_tables, prefill_stride, prefill_batch, max_tiles)
+  hipExtLaunchKernelGGL((mixed_attention_bf16_kernel<D_, GP_, PGP_, MH_, ROT_>), grid,         \
+                        dim3(256), 0, stream, timing_start(), timing_stop(), 0,                \
+                        static_cast<const uint16_t*>(k_cache),                                 \
+                        static_cast<const uint16_t*>(v_cache), num_q_heads, num_kv_heads, G,   \
+                        bs_log2, scale_log2, cos_sin, max_position, n_decode_wg,               \
+                        static_cast<const uint16_t*>(q_decode),                                \
+                        static_cast<uint16_t*>(out_decode), context_lens, decode_tables,       \
+                        decode_stride, decode_batch, n_hg, W, ws.prefix, ws.ml, ws.o,          \
+                        static_cast<const uint16_t*>(q_prefill),                               \
+                        static_cast<uint16_t*>(out_prefill), cu_seqlens_q, cu_seqlens_k,       \
+                        prefill_tables, prefill_stride, prefill_batch, max_tiles)
 #define PKV_MIXED_R(D_, GP_, PGP_, MH_)                   \
   if (cos_sin != nullptr) PKV_MIXED(D_, GP_, PGP_, MH_, true); \
   else PKV_MIXED(D_, GP_, PGP_, MH_, false);

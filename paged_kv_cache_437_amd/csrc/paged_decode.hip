@@ -58,11 +58,13 @@ hipError_t launch_decode_append(const void* q, void* out, const void* k_cache,
   const DecodeWorkspace ws = carve_decode_workspace(workspace, batch, W, MH * GP);
   const float scale_log2 = scale * kLog2e;
   timing_begin("paged_decode_append", stream);
-  hipLaunchKernelGGL((paged_decode_append_bf16_kernel<D, GP, MH>), dim3((W + 3) / 4), dim3(256),
-                     0, stream, static_cast<const uint16_t*>(q), static_cast<uint16_t*>(out),
-                     static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache),
-                     context_lens, block_tables, table_stride, batch, num_q_heads, num_kv_heads, G,
-                     n_hg, bs_log2, scale_log2, W, ws.prefix, ws.ml, ws.o, app);
+  hipExtLaunchKernelGGL((paged_decode_append_bf16_kernel<D, GP, MH>), dim3((W + 3) / 4), dim3(256),
+                        0, stream, timing_start(), timing_stop(), 0,
+                        static_cast<const uint16_t*>(q), static_cast<uint16_t*>(out),
+                        static_cast<const uint16_t*>(k_cache),
+                        static_cast<const uint16_t*>(v_cache), context_lens, block_tables,
+                        table_stride, batch, num_q_heads, num_kv_heads, G, n_hg, bs_log2,
+                        scale_log2, W, ws.prefix, ws.ml, ws.o, app);
   timing_end(stream);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -86,12 +88,12 @@ hipError_t launch_decode(const void* q, void* out, const void* k_cache, const vo
   timing_begin("paged_decode", stream);
   auto kernel = cos_sin != nullptr ? paged_decode_bf16_kernel<D, GP, MH, ONE_BLOCK, true>
                                    : paged_decode_bf16_kernel<D, GP, MH, ONE_BLOCK, false>;
-  hipLaunchKernelGGL(kernel, dim3((W + 3) / 4), dim3(256), 0, stream,
-                     static_cast<const uint16_t*>(q), static_cast<uint16_t*>(out),
-                     static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache),
-                     context_lens, block_tables, table_stride, batch, num_q_heads, num_kv_heads, G,
-                     n_hg, bs_log2, scale_log2, W, ws.prefix, ws.ml, ws.o, cos_sin,
-                     max_position);
+  hipExtLaunchKernelGGL(kernel, dim3((W + 3) / 4), dim3(256), 0, stream, timing_start(),
+                        timing_stop(), 0, static_cast<const uint16_t*>(q),
+                        static_cast<uint16_t*>(out), static_cast<const uint16_t*>(k_cache),
+                        static_cast<const uint16_t*>(v_cache), context_lens, block_tables,
+                        table_stride, batch, num_q_heads, num_kv_heads, G, n_hg, bs_log2,
+                        scale_log2, W, ws.prefix, ws.ml, ws.o, cos_sin, max_position);
   timing_end(stream);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

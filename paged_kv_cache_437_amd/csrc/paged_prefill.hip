@@ -31,11 +31,11 @@ static void launch_prefill(dim3 grid, hipStream_t stream, const void* q, void* o
                                     : paged_prefill_bf16_kernel<D, GP, false, true>)
                     : (bs_log2 >= 6 ? paged_prefill_bf16_kernel<D, GP, true, false>
                                     : paged_prefill_bf16_kernel<D, GP, false, false>);
-  hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream,
-                     static_cast<const uint16_t*>(q), static_cast<uint16_t*>(out),
-                     static_cast<const uint16_t*>(kc), static_cast<const uint16_t*>(vc), cu_q,
-                     cu_k, tables, stride, Hq, Hkv, G, bs_log2, scale_log2, batch, max_tiles,
-                     cos_sin, max_position);
+  hipExtLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, timing_start(), timing_stop(), 0,
+                        static_cast<const uint16_t*>(q), static_cast<uint16_t*>(out),
+                        static_cast<const uint16_t*>(kc), static_cast<const uint16_t*>(vc), cu_q,
+                        cu_k, tables, stride, Hq, Hkv, G, bs_log2, scale_log2, batch, max_tiles,
+                        cos_sin, max_position);
 }
 
 hipError_t launch_paged_prefill_bf16(int head_dim, const void* q, void* out, const void* k_cache,

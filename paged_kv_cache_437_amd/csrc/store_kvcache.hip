@@ -92,10 +92,11 @@ hipError_t launch_store_kvcache_rotary(bool bf16, int head_dim, void* k_cache, v
   const int threads = row_chunks >= 256 ? 256 : ((row_chunks + 63) / 64) * 64;
   timing_begin("store_kvcache_rotary", stream);
 #define PKV_STORE_ROT(T, D)                                                                    \
-  hipLaunchKernelGGL((store_kvcache_rotary_kernel<T, D>), dim3(num_tokens), dim3(threads), 0, \
-                     stream, static_cast<T*>(k_cache), static_cast<uint4*>(v_cache),          \
-                     static_cast<const T*>(k), static_cast<const uint4*>(v), slot_mapping,    \
-                     positions, cos_sin, max_position, num_kv_heads)
+  hipExtLaunchKernelGGL((store_kvcache_rotary_kernel<T, D>), dim3(num_tokens), dim3(threads),  \
+                        0, stream, timing_start(), timing_stop(), 0, static_cast<T*>(k_cache), \
+                        static_cast<uint4*>(v_cache), static_cast<const T*>(k),                \
+                        static_cast<const uint4*>(v), slot_mapping, positions, cos_sin,        \
+                        max_position, num_kv_heads)
   if (bf16) {
     if (head_dim == 64) PKV_STORE_ROT(uint16_t, 64); else PKV_STORE_ROT(uint16_t, 128);
   } else {
@@ -113,10 +114,10 @@ hipError_t launch_store_kvcache(void* k_cache, void* v_cache, const void* k, con
   const int chunks = row_bytes / 16;
   const int threads = chunks >= 256 ? 256 : ((chunks + 63) / 64) * 64;
   timing_begin("store_kvcache", stream);
-  hipLaunchKernelGGL(store_kvcache_kernel, dim3(num_tokens), dim3(threads), 0, stream,
-                     static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache),
-                     static_cast<const uint4*>(k), static_cast<const uint4*>(v), slot_mapping,
-                     chunks);
+  hipExtLaunchKernelGGL(store_kvcache_kernel, dim3(num_tokens), dim3(threads), 0, stream,
+                        timing_start(), timing_stop(), 0, static_cast<uint4*>(k_cache),
+                        static_cast<uint4*>(v_cache), static_cast<const uint4*>(k),
+                        static_cast<const uint4*>(v), slot_mapping, chunks);
   timing_end(stream);
   return hipGetLastError();
 }

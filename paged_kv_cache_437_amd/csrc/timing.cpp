@@ -47,24 +47,34 @@ namespace pkv {
 
 void timing_begin(const char* kernel, hipStream_t stream) {
   if (!g_on.load(std::memory_order_relaxed)) return;
+  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &capture) != hipSuccess ||
+      capture != hipStreamCaptureStatusNone)
+    return;  // launches captured into a graph are not timed
   std::lock_guard<std::mutex> lk(g_mu);
   t_open = {kernel, take_event(), take_event()};
-  // a start event that could not be recorded drops this launch from the timing
-  if (t_open.start && hipEventRecord(t_open.start, stream) != hipSuccess) {
+  // a pair that could not be created in full drops this launch from the timing
+  if (t_open.start == nullptr || t_open.stop == nullptr) {
+    if (t_open.start) g_spare.push_back(t_open.start);
     if (t_open.stop) g_spare.push_back(t_open.stop);
-    g_spare.push_back(t_open.start);
     t_open = {nullptr, nullptr, nullptr};
   }
 }
 
+hipEvent_t timing_start() { return t_open.start; }
+
+hipEvent_t timing_stop() { return t_open.stop; }
+
 void timing_end(hipStream_t stream) {
-  if (!g_on.load(std::memory_order_relaxed) || t_open.kernel == nullptr) return;
+  (void)stream;
+  if (t_open.kernel == nullptr) return;
   std::lock_guard<std::mutex> lk(g_mu);
-  if (t_open.start && t_open.stop && hipEventRecord(t_open.stop, stream) == hipSuccess) {
+  // the launch recorded both events unless it was refused
+  if (hipPeekAtLastError() == hipSuccess) {
     g_pending.push_back(t_open);
   } else {
-    if (t_open.start) g_spare.push_back(t_open.start);
-    if (t_open.stop) g_spare.push_back(t_open.stop);
+    g_spare.push_back(t_open.start);
+    g_spare.push_back(t_open.stop);
   }
   t_open = {nullptr, nullptr, nullptr};
 }

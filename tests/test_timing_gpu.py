@@ -41,3 +41,39 @@ def test_timing_samples_in_launch_order():
     totals = pkv.timing_collect()
     assert sorted(totals) == sorted(set(names))
     assert all(t["launches"] == 2 and t["min_ms"] <= t["max_ms"] for t in totals.values())
+
+
+def test_timing_skips_launches_captured_into_a_graph():
+    """With timing on while a decode step is captured into a HIP graph, the launches
+    made during the capture take no events (only the wrapper's eager warm-up run is
+    timed), and the replays still match the eager step bit for bit."""
+    import paged_kv_cache_437_amd as pkv
+    from paged_kv_cache_437_amd.graphs import DecodeStepGraph
+    from paged_kv_cache_437_amd.step import DeviceStep
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    wl = workloads.custom("timing_graph", "bf16", 8, 8, 128, 16,
+                          [workloads.SeqSpec("decode", L, 1) for L in (40, 300, 17)], seed=4)
+    st = DeviceStep(wl, device="cuda")
+    eager = DeviceStep(wl, device="cuda")
+    torch.cuda.synchronize()
+    pkv.timing_collect()
+    pkv.timing_enable(True)
+    try:
+        g = DecodeStepGraph(st.k_cache, st.v_cache, wl.num_q_heads, 3,
+                            st.decode_tables.shape[1], wl.scale)
+        torch.cuda.synchronize()
+        during = pkv.timing_collect()
+        for _ in range(2):
+            out = g.run(st.q_decode, st.k_new, st.v_new, st.slot_mapping, st.decode_tables,
+                        st.context_lens)
+        torch.cuda.synchronize()
+        replays = pkv.timing_collect()
+    finally:
+        pkv.timing_enable(False)
+    # the warm-up step ran eagerly once: each of its kernels timed once, nothing more
+    assert during and all(t["launches"] == 1 for t in during.values()), during
+    assert replays == {}, replays
+    eager.run()
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), eager.out_decode.view(torch.int16))
+    assert torch.equal(st.k_cache.view(torch.int16), eager.k_cache.view(torch.int16))
