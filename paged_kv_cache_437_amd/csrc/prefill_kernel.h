@@ -203,9 +203,10 @@ __device__ __forceinline__ void prefill_workgroup(
   // two K and two V tile buffers; the tile loop is unrolled by two so every LDS
   // address is a per-lane base plus an immediate
   __shared__ __attribute__((aligned(1024))) char k_lds0[TB];
-  __shared__ __attribute__((aligned(1024))) char k_lds1[TB];
   __shared__ __attribute__((aligned(1024))) char v_lds0[TB];
-  __shared__ __attribute__((aligned(1024))) char v_lds1[TB];
+  __shared__ __attribute__((aligned(1024))) char kv_lds1[2 * TB];  // second K, then second V
+  char* const k_lds1 = kv_lds1;
+  char* const v_lds1 = kv_lds1 + TB;
 
   int b = 0, kvh = 0, tile = 0;
   if (Hkv % kXcds == 0) {
@@ -294,11 +295,20 @@ __device__ __forceinline__ void prefill_workgroup(
     }
   };
 
+  constexpr int KR = ROT ? KS / 2 : 1;
+  constexpr int TROW = D * 4;                              // bytes of one table row
+  constexpr bool STAGE = ROT && BM_TOK * TROW <= 2 * TB;  // q tiles of <= 64 tokens
+  // With the table staged and blocks of 64 or more keys, the table rows and q go out
+  // first and tile 0 after them, so the rotation runs while tile 0 is in flight.
+  constexpr bool ROT_AHEAD = STAGE && BIG_BLOCK;
+
   // tile 0 goes out before the q rows: with blocks of 64 or more keys its block is the
   // table's first entry, loaded with the sequence bounds rather than after them
   int te_next = BIG_BLOCK ? table[0] : 0;
-  fetch(0, te_next, k_lds0, v_lds0);
-  if (BIG_BLOCK && n_kv > 1) te_next = tile_block(1);
+  if constexpr (!ROT_AHEAD) {
+    fetch(0, te_next, k_lds0, v_lds0);
+    if (BIG_BLOCK && n_kv > 1) te_next = tile_block(1);
+  }
 
   // rotary: cosines and sines of this row's position for the elements this lane holds
   // in k-steps ks < KS/2.  When the item's rows of the table (one per token of its q
@@ -308,24 +318,22 @@ __device__ __forceinline__ void prefill_workgroup(
   // own row from global memory instead touches 32 rows per load instruction.  Row r's
   // 16-byte chunk c sits at chunk c ^ (r % 16), so 16 consecutive rows read one logical
   // chunk from distinct banks.
-  constexpr int KR = ROT ? KS / 2 : 1;
-  constexpr int TROW = D * 4;                              // bytes of one table row
-  constexpr bool STAGE = ROT && BM_TOK * TROW <= 2 * TB;  // q tiles of <= 64 tokens
   f32x4_t rc[KR][2], rs[KR][2];
-  if constexpr (STAGE) {
+  auto stage_table = [&]() {
     constexpr int CPT = TROW / 16;          // 16-byte chunks per table row
     constexpr int RPI = 64 / CPT;           // rows per wavefront load instruction
-    constexpr int RH = TB / TROW;           // rows per LDS buffer
     constexpr int NI = (BM_TOK + RPI - 1) / RPI;
     const int pos0 = Lk - Lq + tok0;        // position of the tile's first token
     for (int i = wave; i < NI; i += 4) {    // wavefront-uniform
       const int r = i * RPI + lane / CPT;
       const int c = (lane % CPT) ^ (r & 15);
       const int64_t pos = min(max(pos0 + r, 0), max_position - 1);
-      char* dst = i * RPI < RH ? k_lds1 + i * RPI * TROW : v_lds1 + (i * RPI - RH) * TROW;
-      dma16_ptr(cos_sin + pos * D + 4 * c, lds_addr(dst));
+      dma16_ptr(cos_sin + pos * D + 4 * c, lds_addr(k_lds1 + i * RPI * TROW));
     }
-  } else if constexpr (ROT) {
+  };
+  if constexpr (STAGE && !ROT_AHEAD) {
+    stage_table();
+  } else if constexpr (ROT && !STAGE) {
     const float* cs =
         cos_sin + static_cast<int64_t>(min(max(diag, 0), max_position - 1)) * D + 8 * hi;
 #pragma unroll
@@ -339,21 +347,61 @@ __device__ __forceinline__ void prefill_workgroup(
 
   // q row as the S^T MFMA B operand: lane holds d = ks*16 + 8*hi .. +8
   bf16x8_t qb[KS];
+  if constexpr (ROT_AHEAD) {
+    // every lane loads a row of the sequence (a lane past it the nearest real row, zeroed
+    // once the loads have landed), so no branch around the loads stalls the wave on them
+    // before the table rows and tile 0 go out
+    const int64_t qrow = static_cast<int64_t>(q_begin + min(tok, Lq - 1)) * Hq + kvh * G +
+                         min(head, G - 1);
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    u32x4_t w = {0u, 0u, 0u, 0u};
-    if (row_valid)
-      w = *reinterpret_cast<const u32x4_t*>(
-          q + (static_cast<int64_t>(q_begin + tok) * Hq + hq) * D + ks * 16 + 8 * hi);
-    qb[ks] = __builtin_bit_cast(bf16x8_t, w);
+    for (int ks = 0; ks < KS; ++ks)
+      qb[ks] = __builtin_bit_cast(
+          bf16x8_t, *reinterpret_cast<const u32x4_t*>(q + qrow * D + ks * 16 + 8 * hi));
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4_t w = {0u, 0u, 0u, 0u};
+      if (row_valid)
+        w = *reinterpret_cast<const u32x4_t*>(
+            q + (static_cast<int64_t>(q_begin + tok) * Hq + hq) * D + ks * 16 + 8 * hi);
+      qb[ks] = __builtin_bit_cast(bf16x8_t, w);
+    }
   }
-  if constexpr (STAGE) {
+  if constexpr (ROT_AHEAD) {
+    // q went out first, then the table rows, then tile 0 (the scheduling barriers keep
+    // the compiler from moving loads across); the wait leaves tile 0's 2*LIT
+    // direct-to-LDS loads in flight: vmcnt counts this wave's memory loads in issue
+    // order, so at most 2*LIT outstanding means q and the table rows have landed.  The
+    // barrier is the bare instruction: __syncthreads' release fence would wait for
+    // tile 0 as well.  The empty asm keeps the compiler from moving the table's LDS
+    // reads above it.
+    __builtin_amdgcn_sched_barrier(0);
+    stage_table();
+    __builtin_amdgcn_sched_barrier(0);
+    fetch(0, te_next, k_lds0, v_lds0);
+    __builtin_amdgcn_sched_barrier(0);
+    static_assert(2 * LIT <= 15, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(0x0f70 | (2 * LIT));  // vmcnt(2*LIT)
+    __builtin_amdgcn_s_barrier();  // every wave's table rows have landed
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    if (n_kv > 1) te_next = tile_block(1);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4_t w = __builtin_bit_cast(u32x4_t, qb[ks]);
+      qb[ks] = __builtin_bit_cast(bf16x8_t, row_valid ? w : u32x4_t{0u, 0u, 0u, 0u});
+    }
+  } else if constexpr (STAGE) {
     // the table rows have landed (this wave's loads and everyone's, after the barrier)
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
     __syncthreads();
-    constexpr int RH = TB / TROW;
+  }
+  if constexpr (STAGE) {
     const int r = R - head * BM_TOK;  // this lane's token within the tile
-    const char* row = r < RH ? k_lds1 + r * TROW : v_lds1 + (r - RH) * TROW;
+    // the second K buffer and the second V buffer are one LDS object, so row r is at
+    // r * TROW from its start whichever buffer holds it (read through a per-lane choice
+    // of two objects, the compiler made the table reads wait for tile 0's loads too)
+    const char* row = k_lds1 + r * TROW;
 #pragma unroll
     for (int ks = 0; ks < KR; ++ks)
 #pragma unroll
