@@ -79,18 +79,50 @@ __device__ __forceinline__ i16x4_t lds_read_tr16(const char* p) {
 // P(Y R) = Hkv * sum_b clamp(Y R - (max_tiles - n_b), 0, n_b) items: a binary search on
 // P finds the group, a wavefront scan the sequence.  Returns false for i past the list.
 // Every value is wavefront-uniform.
+// Bounds of a sequence: its first query row, its query and key counts, and the first
+// entry of its block table.
+struct SeqBounds {
+  int q_begin, Lq, Lk, blk0;
+};
+
 template <int R>
 __device__ bool prefill_item(int64_t i, int batch, int Hkv, int bm_tok, int max_tiles,
-                             const int32_t* __restrict__ cu_q, int& b_out, int& kvh_out,
-                             int& tile_out) {
+                             const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
+                             const int32_t* __restrict__ block_tables, int table_stride,
+                             int& b_out, int& kvh_out, int& tile_out, SeqBounds& sb) {
   constexpr int NC = 4;  // chunks of 64 sequences whose tile counts stay in registers
   const int lane = threadIdx.x & 63;
   auto load_tiles = [&](int b) -> int {
     return b < batch ? (cu_q[b + 1] - cu_q[b] + bm_tok - 1) / bm_tok : 0;
   };
-  int nreg[NC];
+  // the first 64 sequences' bounds and first table entries are loaded with their tile
+  // counts, so when the item's sequence is one of them its bounds need no load after
+  // the search (one dependent round trip fewer before the item's first K/V tile)
+  int cq0 = 0, cq1 = 0, ck0 = 0, ck1 = 0, tb0 = 0;
+  if (lane < batch) {
+    cq0 = cu_q[lane];
+    cq1 = cu_q[lane + 1];
+    ck0 = cu_k[lane];
+    ck1 = cu_k[lane + 1];
+    if (table_stride > 0) tb0 = block_tables[static_cast<int64_t>(lane) * table_stride];
+  }
+  // the other chunks' bounds: every load first (a lane past the batch reads the last
+  // sequence's), then the counts, so the loads overlap instead of waiting in turn
+  int qa[NC], qz[NC];
 #pragma unroll
-  for (int c = 0; c < NC; ++c) nreg[c] = load_tiles(64 * c + lane);
+  for (int c = 1; c < NC; ++c) {
+    qa[c] = qz[c] = 0;
+    if (64 * c < batch) {  // wavefront-uniform
+      const int bc = min(64 * c + lane, batch - 1);
+      qa[c] = cu_q[bc];
+      qz[c] = cu_q[bc + 1];
+    }
+  }
+  int nreg[NC];
+  nreg[0] = (cq1 - cq0 + bm_tok - 1) / bm_tok;  // 0 past the batch
+#pragma unroll
+  for (int c = 1; c < NC; ++c)
+    nreg[c] = 64 * c + lane < batch ? (qz[c] - qa[c] + bm_tok - 1) / bm_tok : 0;
   auto tiles_of = [&](int c) -> int {  // this lane's sequence of chunk c
     if (c < NC) {
       int n = nreg[0];
@@ -130,9 +162,21 @@ __device__ bool prefill_item(int64_t i, int batch, int Hkv, int bm_tok, int max_
       const int rr = static_cast<int>(r) - (__builtin_amdgcn_readlane(incl, ln) -
                                             __builtin_amdgcn_readlane(w, ln));
       kvh_out = rr / cnt_b;
-      b_out = 64 * c + ln;
+      const int b = 64 * c + ln;
+      b_out = b;
       const int n_b = __builtin_amdgcn_readlane(n, ln);
       tile_out = max_tiles - 1 - (max(y0, max_tiles - n_b) + (rr - kvh_out * cnt_b));
+      if (c == 0) {
+        sb.q_begin = __builtin_amdgcn_readlane(cq0, ln);
+        sb.Lq = __builtin_amdgcn_readlane(cq1, ln) - sb.q_begin;
+        sb.Lk = __builtin_amdgcn_readlane(ck1, ln) - __builtin_amdgcn_readlane(ck0, ln);
+        sb.blk0 = __builtin_amdgcn_readlane(tb0, ln);
+      } else {
+        sb.q_begin = cu_q[b];
+        sb.Lq = cu_q[b + 1] - sb.q_begin;
+        sb.Lk = cu_k[b + 1] - cu_k[b];
+        sb.blk0 = block_tables[static_cast<int64_t>(b) * table_stride];
+      }
       return true;
     }
     r -= total;
@@ -209,20 +253,22 @@ __device__ __forceinline__ void prefill_workgroup(
   char* const v_lds1 = kv_lds1 + TB;
 
   int b = 0, kvh = 0, tile = 0;
+  SeqBounds sb;
   if (Hkv % kXcds == 0) {
     // the list restricted to kv heads kvh = wg % 8 + 8 m, m < Hkv / 8
     if (!prefill_item<kLevelGroup>(wg / kXcds, batch, Hkv / kXcds, BM_TOK, max_tiles,
-                                         cu_seqlens_q, b, kvh,
-                      tile))
+                                   cu_seqlens_q, cu_seqlens_k, block_tables, table_stride, b,
+                                   kvh, tile, sb))
       return;  // past the list: uniform over the workgroup, before any barrier
     kvh = wg % kXcds + kXcds * kvh;
-  } else if (!prefill_item<kLevelGroup>(wg, batch, Hkv, BM_TOK, max_tiles, cu_seqlens_q, b,
-                                              kvh, tile)) {
+  } else if (!prefill_item<kLevelGroup>(wg, batch, Hkv, BM_TOK, max_tiles, cu_seqlens_q,
+                                        cu_seqlens_k, block_tables, table_stride, b, kvh, tile,
+                                        sb)) {
     return;
   }
-  const int q_begin = cu_seqlens_q[b];
-  const int Lq = cu_seqlens_q[b + 1] - q_begin;
-  const int Lk = cu_seqlens_k[b + 1] - cu_seqlens_k[b];
+  const int q_begin = sb.q_begin;
+  const int Lq = sb.Lq;
+  const int Lk = sb.Lk;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -304,7 +350,7 @@ __device__ __forceinline__ void prefill_workgroup(
 
   // tile 0 goes out before the q rows: with blocks of 64 or more keys its block is the
   // table's first entry, loaded with the sequence bounds rather than after them
-  int te_next = BIG_BLOCK ? table[0] : 0;
+  int te_next = BIG_BLOCK ? sb.blk0 : 0;
   if constexpr (!ROT_AHEAD) {
     fetch(0, te_next, k_lds0, v_lds0);
     if (BIG_BLOCK && n_kv > 1) te_next = tile_block(1);
