@@ -91,16 +91,27 @@ def _rotary_workloads():
         workloads.custom("rot_bf16_gqa8_d128_bs256", "bf16", 16, 2, 128, 256,
                          [S("prefill", 599, 599), S("prefill", 17, 17), S("decode", 600, 1)],
                          seed=26),
+        # 2 q heads per kv head at head_dim 128 with blocks of 256 keys (the varlen
+        # prefill's shape): q tiles of 64 tokens, whose table rows fill both second K/V
+        # buffers, loaded ahead of tile 0; a partial last q tile and a cached prefix
+        workloads.custom("rot_bf16_gqa2_d128_bs256", "bf16", 16, 8, 128, 256,
+                         [S("prefill", 700, 700), S("prefill", 1000, 300), S("decode", 513, 1)],
+                         seed=27),
+        # more than 64 sequences: the item search finds sequences past the first 64,
+        # whose bounds it loads after the search
+        workloads.custom("rot_bf16_gqa2_d128_bs64_many", "bf16", 4, 2, 128, 64,
+                         [S("prefill", 1 + (37 * i) % 90, 1 + (37 * i) % 90) for i in range(70)]
+                         + [S("prefill", 200, 75), S("decode", 130, 1)], seed=28),
     ]
 
 
 # table rows per case: the last case's table ends at its longest context, so the rows
 # of the 599-token prompt's last q tile past its last token (positions 599..607) clamp to
 # the table's last row
-_TABLE_ROWS = [2048, 2048, 2048, 2048, 2048, 600]
+_TABLE_ROWS = [2048, 2048, 2048, 2048, 2048, 600, 2048, 2048]
 
 
-@pytest.mark.parametrize("idx", range(6))
+@pytest.mark.parametrize("idx", range(8))
 def test_rotary_step_parity(idx):
     import paged_kv_cache_437_amd as pkv
     from paged_kv_cache_437_amd.step import DeviceStep
