@@ -65,6 +65,12 @@ __device__ __forceinline__ i16x4_t lds_read_tr16(const char* p) {
       (__attribute__((address_space(3))) i16x4_t*)((const __attribute__((address_space(3))) char*)p));
 }
 
+// Bounds of a sequence: its first query row, its query and key counts, and the first
+// entry of its block table.
+struct SeqBounds {
+  int q_begin, Lq, Lk, blk0;
+};
+
 // Workgroup -> work item.  Q tile j of a sequence (j from 0 at its first query) sits at
 // level u = max_tiles - 1 - j, so the last (heaviest) tiles of the longest prompts come
 // first and tile 0 of every prompt last: in a causal prompt the tiles of one level need
@@ -77,14 +83,8 @@ __device__ __forceinline__ i16x4_t lds_read_tr16(const char* p) {
 // prefix-cached and long prompts within noise; outputs bit-identical.  With n_b q tiles
 // in sequence b (levels max_tiles - n_b .. max_tiles - 1), the groups below Y hold
 // P(Y R) = Hkv * sum_b clamp(Y R - (max_tiles - n_b), 0, n_b) items: a binary search on
-// P finds the group, a wavefront scan the sequence.  Returns false for i past the list.
-// Every value is wavefront-uniform.
-// Bounds of a sequence: its first query row, its query and key counts, and the first
-// entry of its block table.
-struct SeqBounds {
-  int q_begin, Lq, Lk, blk0;
-};
-
+// P finds the group, a wavefront scan the sequence.  Returns false for i past the list,
+// else the item and its sequence's bounds.  Every value is wavefront-uniform.
 template <int R>
 __device__ bool prefill_item(int64_t i, int batch, int Hkv, int bm_tok, int max_tiles,
                              const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
